@@ -1,0 +1,16 @@
+"""Paged decode attention for AMD MI355X (gfx950).
+
+The compute lives in ``libdecode_attn.so`` (hand-written HIP kernels behind a
+C ABI declared in ``include/decode_attn.h``). ``binding`` marshals torch
+tensors into that ABI; nothing in this package computes attention itself.
+"""
+
+from .binding import (  # noqa: F401
+    DecodeAttnError,
+    attn_decode_sliding,
+    attn_decode_global,
+    attn_decode_global_workspace_bytes,
+    attn_status_string,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,198 @@
+"""ctypes binding of ``libdecode_attn.so`` (declared in include/decode_attn.h).
+
+Argument marshalling only: shape and dtype checks on torch tensors, the
+``da_shape`` struct, output/workspace allocation through torch, and the
+current torch stream. Every step of the computation runs in the library's HIP
+kernels; there is no fallback path. If the library is missing the calls raise.
+"""
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+DA_OK = 0
+DA_DTYPE_F32 = 0
+DA_DTYPE_BF16 = 1
+PAGE_SIZE = 16
+
+_lock = threading.Lock()
+_lib = None
+_workspaces = {}
+
+
+class DecodeAttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class DaShape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
+           "attn_status_string")
+
+
+def library_path():
+    return os.environ.get("DECODE_ATTN_LIB", os.path.join(HERE, "lib", "libdecode_attn.so"))
+
+
+def load_library():
+    """Load the shared library (raises DecodeAttnError if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise DecodeAttnError(-100, f"HIP library not built: {path} "
+                                        "(run `python -m decode_attention_amd.build`)")
+        lib = ctypes.CDLL(path)
+        vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+        lib.attn_decode_sliding.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int32, vp,
+                                            ctypes.POINTER(DaShape), vp]
+        lib.attn_decode_sliding.restype = ctypes.c_int32
+        lib.attn_decode_global.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
+                                           ctypes.c_size_t, vp]
+        lib.attn_decode_global.restype = ctypes.c_int32
+        lib.attn_decode_global_workspace_bytes.argtypes = [ctypes.POINTER(DaShape),
+                                                           ctypes.POINTER(ctypes.c_size_t)]
+        lib.attn_decode_global_workspace_bytes.restype = ctypes.c_int32
+        lib.attn_status_string.argtypes = [ctypes.c_int32]
+        lib.attn_status_string.restype = ctypes.c_char_p
+        del i32p
+        _lib = lib
+        return lib
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _check(status):
+    if status != DA_OK:
+        raise DecodeAttnError(status, attn_status_string(status))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return DA_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DA_DTYPE_BF16
+    raise DecodeAttnError(-1, f"unsupported tensor dtype {t.dtype}")
+
+
+def _require(cond, msg):
+    if not cond:
+        raise DecodeAttnError(-1, msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_shape(batch, num_kv_heads, group, head_dim, max_pages_per_seq, num_pages, kv_dtype,
+               num_splits=0):
+    return DaShape(int(batch), int(num_kv_heads), int(group), int(head_dim), PAGE_SIZE,
+                   int(max_pages_per_seq), int(num_pages), int(kv_dtype), DA_DTYPE_F32,
+                   int(num_splits))
+
+
+def _check_common(q, block_table, seq_lens, caches):
+    import torch
+    _require(q.is_cuda and q.dim() == 3 and q.is_contiguous(), "q must be a contiguous cuda [B, Hq, D] tensor")
+    for c in caches:
+        _require(c.is_cuda and c.is_contiguous() and c.device == q.device, "caches must be contiguous, on q's device")
+        _require(c.dtype == q.dtype, "caches must have q's dtype")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+             and block_table.device == q.device, "block_table must be contiguous int32 [B, P_max] on q's device")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1 and seq_lens.is_contiguous()
+             and seq_lens.device == q.device, "seq_lens must be contiguous int32 [B] on q's device")
+    _require(block_table.shape[0] == q.shape[0] and seq_lens.shape[0] == q.shape[0], "batch mismatch")
+
+
+def attn_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out=None, stream=None):
+    """slidingDecodeGQA. q [B, Hkv*G, D]; k_cache, v_cache [P, Hkv, 16, D]
+    (row-major pages); block_table int32 [B, P_max]; seq_lens int32 [B].
+    Returns out fp32 [B, Hkv*G, D] (allocated if not given)."""
+    import torch
+    lib = load_library()
+    _check_common(q, block_table, seq_lens, (k_cache, v_cache))
+    _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape and k_cache.shape[2] == PAGE_SIZE,
+             "k_cache/v_cache must be [P, Hkv, 16, D]")
+    B, Hq, D = q.shape
+    P, Hkv, _, Dk = k_cache.shape
+    _require(Dk == D and Hq % Hkv == 0, "head shape mismatch")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D),
+             "out must be contiguous fp32 [B, Hq, D]")
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q))
+    _check(lib.attn_decode_sliding(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                   _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),
+                                   _stream(stream)))
+    return out
+
+
+def _global_shape(q, kv_cache, block_table, num_splits):
+    B, Hq, D = q.shape
+    _require(kv_cache.dim() == 5 and kv_cache.shape[3] == PAGE_SIZE,
+             "kv_cache must be tiled [P, Hkv, D/x, 16, x]")
+    P, Hkv, nx, _, x = kv_cache.shape
+    _require(nx * x == D and Hq % Hkv == 0, "head shape mismatch")
+    return make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), num_splits)
+
+
+def attn_decode_global_workspace_bytes(shape):
+    n = ctypes.c_size_t(0)
+    _check(load_library().attn_decode_global_workspace_bytes(ctypes.byref(shape), ctypes.byref(n)))
+    return int(n.value)
+
+
+def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=None, num_splits=0,
+                       stream=None):
+    """decodeGQA with values = keys. q [B, Hkv*G, D]; kv_cache tiled
+    [P, Hkv, D/x, 16, x]; returns out fp32 [B, Hkv*G, D]. The workspace is
+    allocated (and cached per device and size) when not given."""
+    import torch
+    lib = load_library()
+    _check_common(q, block_table, seq_lens, (kv_cache,))
+    shape = _global_shape(q, kv_cache, block_table, num_splits)
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D),
+             "out must be contiguous fp32 [B, Hq, D]")
+    need = attn_decode_global_workspace_bytes(shape)
+    if workspace is None and need > 0:
+        key = (q.device, need)
+        workspace = _workspaces.get(key)
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _workspaces[key] = workspace
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                  ctypes.byref(shape), ws_ptr, ws_bytes, _stream(stream)))
+    return out

@@ -1,0 +1,306 @@
+"""Seeded synthetic workloads and the paged KV layouts the kernels read.
+
+This module holds no attention arithmetic. It draws inputs, rounds them to the
+storage dtype and writes them into paged caches through block tables. Tests,
+``bench.py`` and ``smoke()`` use it to feed both the GPU library and the
+oracle.
+
+Input distribution (Model Spec page of gemma-4-12b, "Compute-graph nodes":
+``attn.qk_norm`` is a weighted per-head RMSNorm with eps 1e-6,
+``attn.v_norm`` an unweighted one, both applied before attention):
+
+* every (token, head) row is x ~ N(0, I_D) in float64, then
+  x_hat = x / sqrt(mean(x^2) + 1e-6);
+* q = x_hat * w_q and k = x_hat * w_k, with w_q, w_k ~ N(1, 0.1^2)^D drawn
+  once per layer; v = x_hat (unweighted);
+* global layers have one cache: values equal keys;
+* values are rounded to the storage dtype with round-to-nearest-even (bf16 via
+  binary32, so a rare double rounding is possible; the oracle always reads the
+  stored values, so this does not affect parity).
+
+Each stream has its own generator ``numpy.random.default_rng([tag, layer,
+stream])``: stream 0 seq_lens, 1 block-table permutation, 2 w_q, 3 w_k, 4 q,
+5 k, 6 v.
+
+Paged layouts (page = 16 tokens):
+
+* sliding caches: row-major ``[num_pages][Hkv][16][D]``, one for k, one for v;
+* global cache: tiled ``[num_pages][Hkv][D/x][16][x]``, x = 16 bytes / element
+  size, so 16-byte chunks of x consecutive coordinates are grouped by chunk
+  index first and token second.
+
+Block tables are ``int32 [B][P_max]``; entry j of row b is the physical page of
+logical page j of sequence b. Logical pages in use are numbered in (b, j)
+order and mapped through a seeded permutation of the physical ids. Every other
+entry (padding, and sliding pages wholly before the window) points at a guard
+page, the last physical page, which is filled with NaN; so are the unused slots
+of partly used pages. A kernel that reads outside the visible positions
+therefore produces NaN.
+"""
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+PAGE = 16
+EPS = 1e-6
+BF16_NAN = np.uint16(0x7FC0)
+
+# Gemma-4-12B attention shapes (Model Spec page: "What to watch for" and the
+# attn.core rows of "Compute-graph nodes").
+SLIDING = dict(Hkv=8, G=2, D=256, window=1024)
+GLOBAL = dict(Hkv=1, G=16, D=512)
+
+STREAM_SEQ_LENS, STREAM_PERM, STREAM_WQ, STREAM_WK, STREAM_Q, STREAM_K, STREAM_V = range(7)
+
+
+def rng_for(tag, layer, stream):
+    return np.random.default_rng([int(t) for t in np.atleast_1d(tag)] + [int(layer), int(stream)])
+
+
+# ----------------------------------------------------------------------------
+# storage dtypes
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x):
+    """Round float32 values to bf16 (nearest, ties to even); uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & 0x7FFFFFFF) > 0x7F800000
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
+    out = ((u + r) >> 16).astype(np.uint16)
+    return np.where(nan, BF16_NAN, out)
+
+
+def to_storage(x, kv_dtype):
+    """float64 rows -> stored array (uint16 bf16 bits, or float32)."""
+    if kv_dtype == "bf16":
+        return f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32))
+    if kv_dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+    raise ValueError(kv_dtype)
+
+
+def storage_np_dtype(kv_dtype):
+    return {"bf16": np.uint16, "f32": np.float32}[kv_dtype]
+
+
+def storage_nan(kv_dtype):
+    return BF16_NAN if kv_dtype == "bf16" else np.float32(np.nan)
+
+
+def chunk_elems(kv_dtype):
+    """x of the tiled layout: elements per 16-byte chunk."""
+    return 16 // np.dtype(storage_np_dtype(kv_dtype)).itemsize
+
+
+# ----------------------------------------------------------------------------
+# row generation
+# ----------------------------------------------------------------------------
+
+def rms_rows(rng, shape):
+    """N(0, I) rows (last axis) divided by sqrt(mean(x^2) + 1e-6)."""
+    x = rng.standard_normal(shape)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + EPS)
+
+
+def norm_weight(rng, D):
+    return 1.0 + 0.1 * rng.standard_normal(D)
+
+
+# ----------------------------------------------------------------------------
+# layout scatter
+# ----------------------------------------------------------------------------
+
+def scatter_rowmajor(cache, bt_row, positions, rows):
+    """cache[bt[t // 16], :, t % 16, :] = rows[i] for t = positions[i]."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(bt_row, dtype=np.int64)[positions // PAGE]
+    cache[pages, :, positions % PAGE, :] = rows
+
+
+def scatter_tiled(cache, bt_row, positions, rows):
+    """Tiled layout [P][Hkv][D/x][16][x]: element (t, c, d) goes to
+    cache[bt[t // 16], c, d // x, t % 16, d % x]."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(bt_row, dtype=np.int64)[positions // PAGE]
+    n, hkv, D = rows.shape
+    x = cache.shape[-1]
+    cache[pages, :, :, positions % PAGE, :] = rows.reshape(n, hkv, D // x, x)
+
+
+# ----------------------------------------------------------------------------
+# block tables
+# ----------------------------------------------------------------------------
+
+def build_block_table(page_ranges, P_max, rng):
+    """page_ranges[b] = (j_lo, j_hi): logical pages j_lo..j_hi-1 of sequence b
+    get physical pages. Returns (block_table int32 [B, P_max], num_pages)
+    where the guard page is num_pages - 1."""
+    B = len(page_ranges)
+    counts = [max(0, hi - lo) for lo, hi in page_ranges]
+    n_alloc = int(sum(counts))
+    perm = rng.permutation(n_alloc).astype(np.int64)
+    guard = n_alloc
+    bt = np.full((B, max(int(P_max), 1)), guard, dtype=np.int32)
+    k = 0
+    for b, (lo, hi) in enumerate(page_ranges):
+        if hi > lo:
+            bt[b, lo:hi] = perm[k:k + hi - lo]
+            k += hi - lo
+    return bt, n_alloc + 1
+
+
+def pages_for(L):
+    return (int(L) + PAGE - 1) // PAGE
+
+
+# ----------------------------------------------------------------------------
+# workloads
+# ----------------------------------------------------------------------------
+
+@dataclass
+class SlidingWorkload:
+    q: np.ndarray            # [B, Hkv*G, D] stored
+    k_cache: np.ndarray      # [P, Hkv, 16, D] stored
+    v_cache: np.ndarray
+    block_table: np.ndarray  # int32 [B, P_max]
+    seq_lens: np.ndarray     # int32 [B]
+    window: int
+    kv_dtype: str
+    Hkv: int
+    G: int
+    D: int
+    meta: dict = field(default_factory=dict)
+
+
+@dataclass
+class GlobalWorkload:
+    q: np.ndarray            # [B, Hkv*G, D] stored
+    kv_cache: np.ndarray     # [P, Hkv, D/x, 16, x] stored
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    kv_dtype: str
+    Hkv: int
+    G: int
+    D: int
+    meta: dict = field(default_factory=dict)
+
+
+def make_sliding(seq_lens, *, Hkv=8, G=2, D=256, window=1024, kv_dtype="bf16",
+                 tag=(100,), layer=0, P_max=None, window_only=True,
+                 poison=True, q_scale=1.0, q_zero=False):
+    """Sliding-layer workload. Only the visible positions [max(0, L-w), L) of
+    each sequence are drawn and written; with ``window_only`` only the pages
+    that intersect that range are allocated. ``q_scale`` / ``q_zero`` change
+    the query distribution for diffuse-softmax test cases."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    if P_max is None:
+        P_max = max(1, max((pages_for(L) for L in seq_lens), default=1))
+    ranges = []
+    for L in seq_lens:
+        L = int(L)
+        if L <= 0 or window <= 0:
+            ranges.append((0, 0))
+            continue
+        lo = max(0, L - window)
+        ranges.append((lo // PAGE if window_only else 0, pages_for(L)))
+    bt, num_pages = build_block_table(ranges, P_max, rng_for(tag, layer, STREAM_PERM))
+    dt = storage_np_dtype(kv_dtype)
+    fill = storage_nan(kv_dtype) if poison else dt(0)
+    k_cache = np.full((num_pages, Hkv, PAGE, D), fill, dtype=dt)
+    v_cache = np.full((num_pages, Hkv, PAGE, D), fill, dtype=dt)
+    w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D)
+    w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D)
+    rq, rk, rv = (rng_for(tag, layer, s) for s in (STREAM_Q, STREAM_K, STREAM_V))
+    q = rms_rows(rq, (B, Hkv * G, D)) * w_q * q_scale
+    if q_zero:
+        q = np.zeros_like(q)
+    for b, L in enumerate(seq_lens):
+        L = int(L)
+        if L <= 0 or window <= 0:
+            continue
+        lo = max(0, L - window)
+        pos = np.arange(lo, L)
+        k = rms_rows(rk, (len(pos), Hkv, D)) * w_k
+        v = rms_rows(rv, (len(pos), Hkv, D))
+        scatter_rowmajor(k_cache, bt[b], pos, to_storage(k, kv_dtype))
+        scatter_rowmajor(v_cache, bt[b], pos, to_storage(v, kv_dtype))
+    return SlidingWorkload(to_storage(q, kv_dtype), k_cache, v_cache, bt, seq_lens,
+                           int(window), kv_dtype, Hkv, G, D,
+                           meta=dict(num_pages=num_pages, P_max=int(bt.shape[1])))
+
+
+def make_global(seq_lens, *, Hkv=1, G=16, D=512, kv_dtype="bf16", tag=(200,),
+                layer=0, P_max=None, poison=True, q_scale=1.0, q_zero=False,
+                chunk_tokens=8192):
+    """Global-layer workload: one tiled cache (values equal keys)."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    if P_max is None:
+        P_max = max(1, max((pages_for(L) for L in seq_lens), default=1))
+    ranges = [(0, pages_for(L)) if L > 0 else (0, 0) for L in seq_lens]
+    bt, num_pages = build_block_table(ranges, P_max, rng_for(tag, layer, STREAM_PERM))
+    dt = storage_np_dtype(kv_dtype)
+    x = chunk_elems(kv_dtype)
+    fill = storage_nan(kv_dtype) if poison else dt(0)
+    kv = np.empty((num_pages, Hkv, D // x, PAGE, x), dtype=dt)
+    # Fill only what no token overwrites: the guard page and the unused tail
+    # slots of each sequence's last page.
+    kv[num_pages - 1] = fill
+    w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D)
+    w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D)
+    rq, rk = rng_for(tag, layer, STREAM_Q), rng_for(tag, layer, STREAM_K)
+    q = rms_rows(rq, (B, Hkv * G, D)) * w_q * q_scale
+    if q_zero:
+        q = np.zeros_like(q)
+    for b, L in enumerate(seq_lens):
+        L = int(L)
+        if L <= 0:
+            continue
+        last = pages_for(L) - 1
+        if L % PAGE:
+            kv[bt[b, last], :, :, L % PAGE:, :] = fill
+        for t0 in range(0, L, chunk_tokens):
+            pos = np.arange(t0, min(L, t0 + chunk_tokens))
+            k = rms_rows(rk, (len(pos), Hkv, D)) * w_k
+            scatter_tiled(kv, bt[b], pos, to_storage(k, kv_dtype))
+    return GlobalWorkload(to_storage(q, kv_dtype), kv, bt, seq_lens, kv_dtype, Hkv, G, D,
+                          meta=dict(num_pages=num_pages, P_max=int(bt.shape[1])))
+
+
+# ----------------------------------------------------------------------------
+# named configurations (Gemma-4-12B shapes)
+# ----------------------------------------------------------------------------
+
+def uniform_seq_lens(tag, B, lo, hi):
+    return rng_for(tag, 0, STREAM_SEQ_LENS).integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def loguniform_seq_lens(tag, layer, B, L_max):
+    u = rng_for(tag, layer, STREAM_SEQ_LENS).random(B)
+    return np.maximum(1, np.floor(np.exp(u * np.log(L_max + 1)))).astype(np.int32)
+
+
+CONFIGS = {
+    0: "tiny sliding decode, fp32 KV: B=4, seq_lens {1,17,1024,2048}, Hkv=8, G=2, D=256, window 1024",
+    1: "sliding layer decode, bf16 KV, fp32 accumulate: B=64, seq_lens U[1,32768], Hkv=8, G=2, D=256, window 1024",
+    2: "global layer decode, bf16 K=V: B=64, seq_lens U[1,32768], Hkv=1, G=16, D=512",
+    3: "long-context global decode, bf16 K=V: B=2, seq_lens {131072, 262144}, Hkv=1, G=16, D=512",
+}
+
+
+def config_workload(cfg, layer=0):
+    if cfg == 0:
+        return make_sliding([1, 17, 1024, 2048], kv_dtype="f32", tag=(0,), layer=layer,
+                            P_max=128, **SLIDING)
+    if cfg == 1:
+        sl = uniform_seq_lens((1,), 64, 1, 32768)
+        return make_sliding(sl, kv_dtype="bf16", tag=(1,), layer=layer, P_max=2048, **SLIDING)
+    if cfg == 2:
+        sl = uniform_seq_lens((2,), 64, 1, 32768)
+        return make_global(sl, kv_dtype="bf16", tag=(2,), layer=layer, P_max=2048, **GLOBAL)
+    if cfg == 3:
+        return make_global([131072, 262144], kv_dtype="bf16", tag=(3,), layer=layer,
+                           P_max=16384, **GLOBAL)
+    raise ValueError(cfg)

@@ -1,0 +1,127 @@
+"""Paged-cache front end of the oracle (test infrastructure only).
+
+The pages define the node tensors logically: ``k`` and ``v`` are
+[B, S, Hkv, D] with ``seq_lens`` [B] (Model Spec page, "Tensors of the main
+nodes", ``attn.core`` row), and the shape domain fixes a page size of 16
+("At a glance"). How the cached positions sit in memory is the library's
+choice; this module reads the two layouts the library documents, written here
+from their definitions:
+
+* row-major paged cache ``[num_pages][Hkv][16][D]`` (sliding layers, separate
+  k and v caches): token t of sequence b, KV head c, coordinate d is
+  ``cache[bt[b, t // 16], c, t % 16, d]``;
+* tiled paged cache ``[num_pages][Hkv][D / x][16][x]`` with x = 16 bytes /
+  element size (global layers, one cache read as both k and v): the same
+  element is ``cache[bt[b, t // 16], c, d // x, t % 16, d % x]``.
+
+Stored values are decoded exactly to float64 (bf16 bit patterns are the top
+16 bits of an IEEE binary32 value).
+"""
+
+import numpy as np
+
+from .attention import decode_gqa, sliding_decode_gqa
+
+PAGE = 16  # tokens per page (Model Spec page, "At a glance", shape domain)
+
+
+def stored_to_f64(a, kv_dtype):
+    """Exact float64 value of stored elements.
+
+    kv_dtype "bf16": ``a`` holds uint16 bit patterns; "f32": ``a`` is float32.
+    """
+    a = np.asarray(a)
+    if kv_dtype == "bf16":
+        assert a.dtype == np.uint16
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if kv_dtype == "f32":
+        assert a.dtype == np.float32
+        return a.astype(np.float64)
+    raise ValueError(kv_dtype)
+
+
+def gather_rowmajor_cache(cache, bt_row, positions):
+    """Rows k[t, :, :] ([n, Hkv, D], stored dtype) of a row-major paged cache
+    for the logical positions ``positions`` of one sequence."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(bt_row, dtype=np.int64)[positions // PAGE]
+    slots = positions % PAGE
+    return cache[pages, :, slots, :]
+
+
+def gather_tiled_cache(cache, bt_row, positions):
+    """Rows k[t, :, :] ([n, Hkv, D], stored dtype) of a tiled paged cache
+    ``[num_pages][Hkv][D/x][16][x]`` for the logical positions given."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(bt_row, dtype=np.int64)[positions // PAGE]
+    slots = positions % PAGE
+    sub = cache[pages, :, :, slots, :]          # [n, Hkv, D/x, x]
+    n, hkv, nx, x = sub.shape
+    return sub.reshape(n, hkv, nx * x)
+
+
+def sliding_visible_range(L, window):
+    """Positions visible to the decode query of a sequence of L cached tokens
+    under the sliding window: l <= L-1 and L-1 < l + window, i.e. the half-open
+    range [max(0, L - window), L) (empty when window = 0 or L = 0)."""
+    L = int(L)
+    window = int(window)
+    if L <= 0 or window <= 0:
+        return 0, 0
+    return max(0, L - window), L
+
+
+def paged_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window,
+                         kv_dtype, scale=1.0):
+    """Sliding-window decode node (``attn.core`` on sliding layers):
+    o[b, h] = sum over the last ``window`` positions of softmax(scale * <q[b,h],
+    k[b,s,h // G]>) * v[b,s,h // G].
+
+    q : [B, Hkv*G, D] stored; k_cache, v_cache : row-major paged caches;
+    returns float64 [B, Hkv*G, D].
+
+    Only the visible positions are gathered. Every other position has weight
+    exactly 0 in the definition, so leaving it out does not change the value;
+    it also means storage outside the window is never read (it may hold
+    anything, including NaN).
+    """
+    qf = stored_to_f64(q, kv_dtype)
+    B, Hq, D = qf.shape
+    Hkv = k_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        lo, hi = sliding_visible_range(seq_lens[b], window)
+        if hi <= lo:
+            continue  # nothing visible: the output row stays 0
+        pos = np.arange(lo, hi)
+        k = stored_to_f64(gather_rowmajor_cache(k_cache, block_table[b], pos), kv_dtype)
+        v = stored_to_f64(gather_rowmajor_cache(v_cache, block_table[b], pos), kv_dtype)
+        # The gathered keys are the last (hi - lo) <= window positions, so on
+        # them slidingDecodeGQA sees every key.
+        o = sliding_decode_gqa(scale, window, qf[b].reshape(Hkv, G, D), k, v)
+        out[b] = o.reshape(Hq, D)
+    return out
+
+
+def paged_decode_global(q, kv_cache, block_table, seq_lens, kv_dtype, scale=1.0):
+    """Global decode node (``attn.core`` on global layers, ``decodeGQA``):
+    every cached position is visible and values equal keys, so one tiled cache
+    supplies both k and v.
+
+    q : [B, Hkv*G, D] stored; kv_cache : tiled paged cache; returns float64
+    [B, Hkv*G, D].
+    """
+    qf = stored_to_f64(q, kv_dtype)
+    B, Hq, D = qf.shape
+    Hkv = kv_cache.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        k = stored_to_f64(gather_tiled_cache(kv_cache, block_table[b], np.arange(L)), kv_dtype)
+        o = decode_gqa(scale, qf[b].reshape(Hkv, G, D), k, k)
+        out[b] = o.reshape(Hq, D)
+    return out
