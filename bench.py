@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+One step = one pass of the hot path over one batch at Gemma-4-12B shapes,
+B = 64, seq_lens uniform in [1, 32768] (bf16 KV, fp32 accumulate and output):
+  * attn_decode_sliding: sliding layer, 16 q heads on 8 KV heads, D = 256,
+    window 1024, separate k/v caches (row-major pages);
+  * attn_decode_global: global layer, 16 q heads on 1 KV head, D = 512,
+    values = keys (tiled pages), split over workgroups + log-sum-exp merge.
+Inputs are generated on the host, copied to HBM once, and are resident
+before the timed region. The metric is achieved HBM GB/s over the algorithmic
+bytes (KV read once, K=V counted once, plus q, out and block-table entries)
+and microseconds per layer call.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def sliding_bytes(wl):
+    import numpy as np
+    esize = 2 if wl.kv_dtype == "bf16" else 4
+    L = wl.seq_lens.astype(np.int64)
+    vis = np.minimum(L, wl.window)
+    kv = int(vis.sum()) * wl.Hkv * wl.D * 2 * esize
+    B, Hq = len(L), wl.Hkv * wl.G
+    lo = np.maximum(L - wl.window, 0)
+    pages = np.where(vis > 0, (L - 1) // 16 - lo // 16 + 1, 0)
+    return dict(kv=kv, q=B * Hq * wl.D * esize, out=B * Hq * wl.D * 4,
+                table=int(pages.sum()) * 4 + B * 4)
+
+
+def global_bytes(wl):
+    import numpy as np
+    esize = 2 if wl.kv_dtype == "bf16" else 4
+    L = wl.seq_lens.astype(np.int64)
+    B, Hq = len(L), wl.Hkv * wl.G
+    return dict(kv=int(L.sum()) * wl.Hkv * wl.D * esize, q=B * Hq * wl.D * esize,
+                out=B * Hq * wl.D * 4, table=int(((L + 15) // 16).sum()) * 4 + B * 4)
+
+
+def to_dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(sl, gl, sl_bytes_fn, gl_bytes_fn, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    done_b = 0
+    t_total = 0.0
+    # sliding: sequences in order until a third of the budget is used
+    ns = 0
+    t0 = time.perf_counter()
+    while ns < len(sl.seq_lens) and time.perf_counter() - t0 < budget_s / 3:
+        r = slice(ns, ns + 4)
+        oracle.paged_decode_sliding(sl.q[r], sl.k_cache, sl.v_cache, sl.block_table[r], sl.seq_lens[r],
+                                    sl.window, sl.kv_dtype)
+        ns = min(ns + 4, len(sl.seq_lens))
+    t_sl = time.perf_counter() - t0
+    sub = type(sl)(sl.q[:ns], sl.k_cache, sl.v_cache, sl.block_table[:ns], sl.seq_lens[:ns], sl.window,
+                   sl.kv_dtype, sl.Hkv, sl.G, sl.D)
+    done_b += sum(sl_bytes_fn(sub).values())
+    ng = 0
+    t0 = time.perf_counter()
+    while ng < len(gl.seq_lens) and time.perf_counter() - t0 < 2 * budget_s / 3:
+        r = slice(ng, ng + 1)
+        oracle.paged_decode_global(gl.q[r], gl.kv_cache, gl.block_table[r], gl.seq_lens[r], gl.kv_dtype)
+        ng += 1
+    t_gl = time.perf_counter() - t0
+    sub = type(gl)(gl.q[:ng], gl.kv_cache, gl.block_table[:ng], gl.seq_lens[:ng], gl.kv_dtype,
+                   gl.Hkv, gl.G, gl.D)
+    done_b += sum(gl_bytes_fn(sub).values())
+    t_total = t_sl + t_gl
+    return {
+        "value": round(done_b / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{ns} of 64 sliding sequences ({t_sl:.1f} s) and {ng} of 64 global sequences "
+                   f"({t_gl:.1f} s) of the same workload, fp64 NumPy, algorithmic bytes / wall time"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--num-splits", type=int, default=0, help="global kernel workgroups (0 = auto)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, copy this many MiB device-to-device once, so that a "
+                         "counter profile holds a plain copy of known size to scale HBM counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import decode_attention_amd as da
+    from decode_attention_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if not os.path.exists(da.library_path()):
+        from decode_attention_amd.build import build
+        build()
+    da.load_library()
+
+    log("generating config 1 (sliding) and config 2 (global) inputs on the host")
+    t = time.perf_counter()
+    sl = I.config_workload(1)
+    gl = I.config_workload(2)
+    log(f"generated in {time.perf_counter() - t:.1f} s; copying to HBM")
+    d_sl = [to_dev(x) for x in (sl.q, sl.k_cache, sl.v_cache, sl.block_table, sl.seq_lens)]
+    d_gl = [to_dev(x) for x in (gl.q, gl.kv_cache, gl.block_table, gl.seq_lens)]
+    out_sl = torch.empty((64, 16, 256), dtype=torch.float32, device="cuda")
+    out_gl = torch.empty((64, 16, 512), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step():
+        da.attn_decode_sliding(*d_sl[:5], sl.window, out=out_sl)
+        da.attn_decode_global(*d_gl, out=out_gl, num_splits=args.num_splits)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        da.attn_decode_sliding(*d_sl[:5], sl.window, out=out_sl)
+        e[1].record()
+        da.attn_decode_global(*d_gl, out=out_gl, num_splits=args.num_splits)
+        e[2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sl_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    gl_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    log(f"timed: sliding {sl_ms * 1e3:.1f} us/call, global {gl_ms * 1e3:.1f} us/call, "
+        f"wall {wall / args.steps * 1e3:.3f} ms/step")
+
+    sb, gb = sliding_bytes(sl), global_bytes(gl)
+    step_bytes = sum(sb.values()) + sum(gb.values())
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    g_ach = sum(gb.values()) / (gl_ms * 1e-3) / 1e9
+    s_ach = sum(sb.values()) / (sl_ms * 1e-3) / 1e9
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration_mib} MiB device-to-device for counter calibration")
+        del src, dst
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"timing the oracle on a bounded sample (~{args.cpu_budget:.0f} s)")
+        cpu = cpu_baseline(sl, gl, sliding_bytes, global_bytes, args.cpu_budget)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": ("gemma4-12b decode attention, B=64, seq_lens U[1,32768]: one sliding-layer call "
+                         "(Hkv=8, G=2, D=256, window 1024) + one global-layer call (Hkv=1, G=16, D=512, K=V)"),
+            "global_batch": 64,
+            "seq_len": "U[1,32768]",
+            "parallelism": "single GPU",
+            "sliding_us_per_call": round(sl_ms * 1e3, 2),
+            "global_us_per_call": round(gl_ms * 1e3, 2),
+            "sliding_GBps": round(s_ach, 1),
+            "global_GBps": round(g_ach, 1),
+            "sliding_frac_of_peak": round(s_ach / HBM_PEAK_GBS, 4),
+            "global_frac_of_peak": round(g_ach / HBM_PEAK_GBS, 4),
+            "bytes_per_step": step_bytes,
+            "num_splits": args.num_splits,
+        },
+        "roofline": {
+            "kernel": "attn_decode_global (global_decode_kernel + lse_merge_kernel)",
+            "bound": "hbm",
+            "achieved": round(g_ach, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(g_ach / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

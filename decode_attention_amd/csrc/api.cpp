@@ -1,0 +1,132 @@
+// C ABI of the decode-attention library: host validation, device checks and
+// dispatch to the kernel launchers. Declarations and the contract of every
+// entry point are in include/decode_attn.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kGlobalMaxBatch = 1024;   // per-call prefix table held in LDS
+constexpr int kGlobalMaxSplits = 1 << 16;
+
+struct DeviceInfo {
+  std::atomic<int> state{0};  // 0 unknown, 1 gfx950, -1 unsupported
+  int num_cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Current device if it is a gfx950, else a status. Only called after the
+// host-side argument checks.
+da_status current_device(int* dev_out, int* num_cus) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return DA_ERR_NO_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DA_ERR_NO_DEVICE;
+  DeviceInfo& di = g_dev[dev];
+  if (di.state.load(std::memory_order_acquire) == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (di.state.load(std::memory_order_relaxed) == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DA_ERR_NO_DEVICE;
+      const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      di.num_cus = prop.multiProcessorCount;
+      di.state.store(ok ? 1 : -1, std::memory_order_release);
+    }
+  }
+  if (di.state.load(std::memory_order_acquire) != 1) return DA_ERR_NO_DEVICE;
+  *dev_out = dev;
+  *num_cus = di.num_cus;
+  return DA_OK;
+}
+
+da_status check_common(const da_shape* s) {
+  if (!s) return DA_ERR_INVALID_ARG;
+  if (s->batch <= 0 || s->num_kv_heads <= 0 || s->group <= 0 || s->head_dim <= 0 ||
+      s->max_pages_per_seq <= 0 || s->num_pages <= 0 || s->page_size <= 0 || s->num_splits < 0)
+    return DA_ERR_INVALID_ARG;
+  if (s->kv_dtype != DA_DTYPE_F32 && s->kv_dtype != DA_DTYPE_BF16) return DA_ERR_INVALID_ARG;
+  if (s->out_dtype != DA_DTYPE_F32 && s->out_dtype != DA_DTYPE_BF16) return DA_ERR_INVALID_ARG;
+  if ((long long)s->max_pages_per_seq * s->page_size > (1LL << 30)) return DA_ERR_INVALID_ARG;
+  if (s->page_size != da::kPageSizeAbi) return DA_ERR_UNSUPPORTED;
+  if (s->out_dtype != DA_DTYPE_F32) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+da_status check_global_shape(const da_shape* s) {
+  da_status st = check_common(s);
+  if (st != DA_OK) return st;
+  if (s->num_kv_heads != 1 || s->group != 16 || s->head_dim != 512 || s->kv_dtype != DA_DTYPE_BF16)
+    return DA_ERR_UNSUPPORTED;
+  if (s->batch > kGlobalMaxBatch || s->num_splits > kGlobalMaxSplits) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t window,
+                              void* out, const da_shape* shape, void* stream) {
+  da_status st = check_common(shape);
+  if (st != DA_OK) return st;
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
+  if (window < 0) return DA_ERR_INVALID_ARG;
+  if (shape->group != 2 || shape->head_dim != 256) return DA_ERR_UNSUPPORTED;
+  if ((long long)shape->batch * shape->num_kv_heads > 0x7FFFFFFFLL) return DA_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  return da::launch_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out, *shape,
+                            (hipStream_t)stream);
+}
+
+da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* bytes) {
+  if (!bytes) return DA_ERR_INVALID_ARG;
+  da_status st = check_global_shape(shape);
+  if (st != DA_OK) return st;
+  int dev = 0, cus = 0;
+  if (shape->num_splits == 0) {
+    st = current_device(&dev, &cus);
+    if (st != DA_OK) return st;
+  }
+  *bytes = da::global_workspace_bytes(*shape, da::global_num_splits(*shape, cus));
+  return DA_OK;
+}
+
+da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, const da_shape* shape,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  da_status st = check_global_shape(shape);
+  if (st != DA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  const int splits = da::global_num_splits(*shape, cus);
+  const size_t need = da::global_workspace_bytes(*shape, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
+  return da::launch_global(q, kv_cache, block_table, seq_lens, out, *shape, splits, workspace,
+                           (hipStream_t)stream);
+}
+
+const char* attn_status_string(da_status status) {
+  switch (status) {
+    case DA_OK: return "ok";
+    case DA_ERR_INVALID_ARG: return "invalid argument";
+    case DA_ERR_UNSUPPORTED: return "unsupported shape, dtype or page size";
+    case DA_ERR_WORKSPACE: return "workspace missing or too small";
+    case DA_ERR_NO_DEVICE: return "no gfx950 HIP device is current";
+    case DA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

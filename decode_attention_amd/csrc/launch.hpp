@@ -1,0 +1,25 @@
+// Internal launcher interface between the C ABI (api.cpp) and the kernels.
+// Every launcher assumes the arguments already passed host validation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/decode_attn.h"
+
+namespace da {
+
+constexpr int kPageSizeAbi = 16;  // tokens per page the kernels are built for
+
+da_status launch_sliding(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t window, void* out,
+                         const da_shape& s, hipStream_t stream);
+
+// Number of workgroups the global kernel divides the batch's pages among.
+int global_num_splits(const da_shape& s, int num_cus);
+size_t global_workspace_bytes(const da_shape& s, int num_splits);
+
+da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, void* out, const da_shape& s, int num_splits,
+                        void* workspace, hipStream_t stream);
+
+}  // namespace da

@@ -9,7 +9,7 @@ Input distribution (Model Spec page of gemma-4-12b, "Compute-graph nodes":
 ``attn.qk_norm`` is a weighted per-head RMSNorm with eps 1e-6,
 ``attn.v_norm`` an unweighted one, both applied before attention):
 
-* every (token, head) row is x ~ N(0, I_D) in float64, then
+* every (token, head) row is x ~ N(0, I_D) (drawn in float32), then
   x_hat = x / sqrt(mean(x^2) + 1e-6);
 * q = x_hat * w_q and k = x_hat * w_k, with w_q, w_k ~ N(1, 0.1^2)^D drawn
   once per layer; v = x_hat (unweighted);
@@ -19,8 +19,9 @@ Input distribution (Model Spec page of gemma-4-12b, "Compute-graph nodes":
   stored values, so this does not affect parity).
 
 Each stream has its own generator ``numpy.random.default_rng([tag, layer,
-stream])``: stream 0 seq_lens, 1 block-table permutation, 2 w_q, 3 w_k, 4 q,
-5 k, 6 v.
+stream])``: stream 0 seq_lens, 1 block-table permutation, 2 w_q, 3 w_k, 4 q;
+the k and v rows of sequence b come from ``[tag, layer, 5, b]`` and
+``[tag, layer, 6, b]`` so that sequences can be drawn in parallel threads.
 
 Paged layouts (page = 16 tokens):
 
@@ -38,6 +39,8 @@ of partly used pages. A kernel that reads outside the visible positions
 therefore produces NaN.
 """
 
+import concurrent.futures
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -55,7 +58,8 @@ STREAM_SEQ_LENS, STREAM_PERM, STREAM_WQ, STREAM_WK, STREAM_Q, STREAM_K, STREAM_V
 
 
 def rng_for(tag, layer, stream):
-    return np.random.default_rng([int(t) for t in np.atleast_1d(tag)] + [int(layer), int(stream)])
+    return np.random.default_rng([int(t) for t in np.atleast_1d(tag)] + [int(layer)]
+                                 + [int(s) for s in np.atleast_1d(stream)])
 
 
 # ----------------------------------------------------------------------------
@@ -72,11 +76,11 @@ def f32_to_bf16_bits(x):
 
 
 def to_storage(x, kv_dtype):
-    """float64 rows -> stored array (uint16 bf16 bits, or float32)."""
+    """Real rows -> stored array (uint16 bf16 bits, or float32)."""
     if kv_dtype == "bf16":
-        return f32_to_bf16_bits(np.asarray(x, dtype=np.float64).astype(np.float32))
+        return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
     if kv_dtype == "f32":
-        return np.asarray(x, dtype=np.float64).astype(np.float32)
+        return np.asarray(x, dtype=np.float32)
     raise ValueError(kv_dtype)
 
 
@@ -97,10 +101,25 @@ def chunk_elems(kv_dtype):
 # row generation
 # ----------------------------------------------------------------------------
 
-def rms_rows(rng, shape):
-    """N(0, I) rows (last axis) divided by sqrt(mean(x^2) + 1e-6)."""
-    x = rng.standard_normal(shape)
-    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + EPS)
+def rms_rows(rng, shape, weight=None):
+    """float32 N(0, I) rows (last axis) divided by sqrt(mean(x^2) + 1e-6),
+    then multiplied by ``weight`` (one D-vector) if given."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    ms = np.einsum("...d,...d->...", x, x) / np.float32(shape[-1])
+    x *= (1.0 / np.sqrt(ms + np.float32(EPS)))[..., None]
+    if weight is not None:
+        x *= np.asarray(weight, dtype=np.float32)
+    return x
+
+
+def _parallel(fn, items, workers=None):
+    items = list(items)
+    if workers is None:
+        workers = min(16, len(os.sched_getaffinity(0)))
+    if workers <= 1 or len(items) <= 1:
+        return [fn(i) for i in items]
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(fn, items))
 
 
 def norm_weight(rng, D):
@@ -212,20 +231,21 @@ def make_sliding(seq_lens, *, Hkv=8, G=2, D=256, window=1024, kv_dtype="bf16",
     v_cache = np.full((num_pages, Hkv, PAGE, D), fill, dtype=dt)
     w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D)
     w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D)
-    rq, rk, rv = (rng_for(tag, layer, s) for s in (STREAM_Q, STREAM_K, STREAM_V))
-    q = rms_rows(rq, (B, Hkv * G, D)) * w_q * q_scale
+    q = rms_rows(rng_for(tag, layer, STREAM_Q), (B, Hkv * G, D), w_q) * np.float32(q_scale)
     if q_zero:
         q = np.zeros_like(q)
-    for b, L in enumerate(seq_lens):
-        L = int(L)
+
+    def fill(b):
+        L = int(seq_lens[b])
         if L <= 0 or window <= 0:
-            continue
-        lo = max(0, L - window)
-        pos = np.arange(lo, L)
-        k = rms_rows(rk, (len(pos), Hkv, D)) * w_k
-        v = rms_rows(rv, (len(pos), Hkv, D))
+            return
+        pos = np.arange(max(0, L - window), L)
+        k = rms_rows(rng_for(tag, layer, [STREAM_K, b]), (len(pos), Hkv, D), w_k)
         scatter_rowmajor(k_cache, bt[b], pos, to_storage(k, kv_dtype))
+        v = rms_rows(rng_for(tag, layer, [STREAM_V, b]), (len(pos), Hkv, D))
         scatter_rowmajor(v_cache, bt[b], pos, to_storage(v, kv_dtype))
+
+    _parallel(fill, range(B))
     return SlidingWorkload(to_storage(q, kv_dtype), k_cache, v_cache, bt, seq_lens,
                            int(window), kv_dtype, Hkv, G, D,
                            meta=dict(num_pages=num_pages, P_max=int(bt.shape[1])))
@@ -250,21 +270,23 @@ def make_global(seq_lens, *, Hkv=1, G=16, D=512, kv_dtype="bf16", tag=(200,),
     kv[num_pages - 1] = fill
     w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D)
     w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D)
-    rq, rk = rng_for(tag, layer, STREAM_Q), rng_for(tag, layer, STREAM_K)
-    q = rms_rows(rq, (B, Hkv * G, D)) * w_q * q_scale
+    q = rms_rows(rng_for(tag, layer, STREAM_Q), (B, Hkv * G, D), w_q) * np.float32(q_scale)
     if q_zero:
         q = np.zeros_like(q)
-    for b, L in enumerate(seq_lens):
-        L = int(L)
+
+    def fill_seq(b):
+        L = int(seq_lens[b])
         if L <= 0:
-            continue
-        last = pages_for(L) - 1
+            return
         if L % PAGE:
-            kv[bt[b, last], :, :, L % PAGE:, :] = fill
+            kv[bt[b, pages_for(L) - 1], :, :, L % PAGE:, :] = fill
+        rk = rng_for(tag, layer, [STREAM_K, b])
         for t0 in range(0, L, chunk_tokens):
             pos = np.arange(t0, min(L, t0 + chunk_tokens))
-            k = rms_rows(rk, (len(pos), Hkv, D)) * w_k
+            k = rms_rows(rk, (len(pos), Hkv, D), w_k)
             scatter_tiled(kv, bt[b], pos, to_storage(k, kv_dtype))
+
+    _parallel(fill_seq, range(B))
     return GlobalWorkload(to_storage(q, kv_dtype), kv, bt, seq_lens, kv_dtype, Hkv, G, D,
                           meta=dict(num_pages=num_pages, P_max=int(bt.shape[1])))
 

@@ -1,0 +1,144 @@
+/*
+ * decode_attn.h - C ABI of a paged decode-attention library for AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * What is computed (pages: Op Specs of google/gemma-4-12B, Attention.lean, and
+ * the gemma-4-12b Model Spec, "Compute-graph nodes" attn.core rows):
+ *
+ *   for every sequence b and query head h = c*G + g (KV head c = h / G):
+ *     o[b,h,:] = sum over visible positions l of
+ *                softmax_l( 1 * <q[b,h,:], k[b,l,c,:]> ) * v[b,l,c,:]
+ *
+ *   - attn_decode_sliding: slidingDecodeGQA. The query sits at the last
+ *     position L-1 of the L = seq_lens[b] cached tokens and sees the keys with
+ *     L-1-window < l <= L-1 (slidingGQA's "p - w < l <= p"), i.e. exactly
+ *     min(L, window) keys. Separate k and v caches.
+ *   - attn_decode_global: decodeGQA. Every cached position is visible, and
+ *     values equal keys ("values = keys" on the global layers), so one cache
+ *     is read as both k and v. Long sequences are split over workgroups and
+ *     the per-split results are merged with their log-sum-exp values inside
+ *     the call.
+ *
+ *   The softmax scale is fixed at 1 (the q/k norms take its place on this
+ *   model), so it is not an argument. A sequence with no visible key
+ *   (L = 0, or window = 0) gets an all-zero output row.
+ *
+ * Paged KV layout (page = 16 tokens, the model's page size):
+ *   block_table : int32 [batch][max_pages_per_seq], row-major. Entry j of row
+ *                 b is the physical page that holds tokens 16j .. 16j+15 of
+ *                 sequence b. Only the entries a call needs are read:
+ *                 sliding reads j in [max(0,L-window)/16, (L-1)/16], global
+ *                 reads j in [0, (L-1)/16]. Other entries may hold anything.
+ *   sliding caches (k_cache, v_cache): row-major [num_pages][Hkv][16][D];
+ *                 token t of sequence b, KV head c, coordinate d is element
+ *                 [block_table[b][t/16]][c][t%16][d].
+ *   global cache (kv_cache): tiled [num_pages][Hkv][D/x][16][x], where
+ *                 x = 16 bytes / element size (8 for bf16, 4 for fp32); the
+ *                 same element is [block_table[b][t/16]][c][d/x][t%16][d%x].
+ *                 Each 16-byte chunk holds x consecutive coordinates of one
+ *                 token; chunks are ordered by coordinate group, then token.
+ *   Slots and pages outside the visible positions are never read; they may
+ *   hold any bits, NaN included.
+ *
+ *   q   : [batch][Hkv*G][D], same dtype as the caches.
+ *   out : [batch][Hkv*G][D], fp32.
+ *
+ * Conventions:
+ *   - Every pointer argument except `shape` and `stream` is a device pointer
+ *     owned by the caller. The library reads q, the caches, block_table and
+ *     seq_lens, writes out (and the workspace), and keeps no pointer after
+ *     the call returns.
+ *   - Calls are asynchronous: they validate on the host, enqueue kernels on
+ *     `stream` (a hipStream_t; NULL = the device's null stream) and return.
+ *     Results are valid after the stream is synchronised. Calls hold no
+ *     global state and may be made from several host threads.
+ *   - Host-side validation happens before any HIP call; a non-zero status
+ *     means nothing was enqueued.
+ *   - Preconditions the library cannot check without a device sync (the
+ *     caller's responsibility): 0 <= seq_lens[b] <= 16*max_pages_per_seq,
+ *     every block-table entry a call reads is in [0, num_pages), and out does
+ *     not overlap any input. Violating them is undefined behaviour.
+ *   - The workspace of attn_decode_global must not be shared by two calls
+ *     that may run concurrently.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t da_status;
+
+#define DA_OK 0
+#define DA_ERR_INVALID_ARG (-1) /* null pointer, non-positive size, bad window ... */
+#define DA_ERR_UNSUPPORTED (-2) /* valid but not built: other (Hkv, G, D), dtype, page size */
+#define DA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required */
+#define DA_ERR_NO_DEVICE (-4)   /* no HIP device, or the current device is not gfx950 */
+#define DA_ERR_LAUNCH (-5)      /* a HIP launch reported an error */
+
+#define DA_DTYPE_F32 0
+#define DA_DTYPE_BF16 1
+
+/* Problem description. Host memory, read during the call only. */
+typedef struct da_shape {
+  int32_t batch;             /* B >= 1 sequences */
+  int32_t num_kv_heads;      /* Hkv */
+  int32_t group;             /* G query heads per KV head (Hq = Hkv*G) */
+  int32_t head_dim;          /* D */
+  int32_t page_size;         /* tokens per page; must be 16 */
+  int32_t max_pages_per_seq; /* P_max >= 1: length of a block-table row */
+  int32_t num_pages;         /* physical pages in the cache pool, >= 1 */
+  int32_t kv_dtype;          /* DA_DTYPE_F32 or DA_DTYPE_BF16 (q, k, v) */
+  int32_t out_dtype;         /* DA_DTYPE_F32 */
+  int32_t num_splits;        /* attn_decode_global: number of workgroups the
+                                cached pages of the whole batch are divided
+                                among (0 = one per compute unit); ignored by
+                                attn_decode_sliding */
+} da_shape;
+
+/*
+ * slidingDecodeGQA over paged k/v caches (Gemma-4-12B sliding layers:
+ * Hkv = 8, G = 2, D = 256, window 1024).
+ *   Built shapes: (Hkv, G, D) with G = 2, D = 256, any Hkv >= 1;
+ *   kv dtypes fp32 and bf16; out fp32.
+ *   window >= 0 (0 gives zeros). seq_lens: int32 [batch].
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_NO_DEVICE or
+ * DA_ERR_LAUNCH.
+ */
+da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              int32_t window, void* out, const da_shape* shape, void* stream);
+
+/*
+ * Bytes of device workspace attn_decode_global needs for `shape` on the
+ * current device (per-split partial results: for each of 2*num_splits slots,
+ * Hq*(D+2) fp32 values). Writes the size to *bytes.
+ */
+da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* bytes);
+
+/*
+ * decodeGQA over a paged K=V cache (Gemma-4-12B global layers: Hkv = 1,
+ * G = 16, D = 512, values equal keys).
+ *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32.
+ *   workspace: device memory of at least attn_decode_global_workspace_bytes
+ *   (may be NULL when that size is 0). Its contents need no initialisation
+ *   and are meaningless after the call.
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE,
+ * DA_ERR_NO_DEVICE or DA_ERR_LAUNCH.
+ */
+da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, void* out, const da_shape* shape,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_string(da_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

@@ -1,0 +1,113 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/decode_attn.h declares, and host validation returns the documented
+status codes before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_amd as da
+from decode_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(da.library_path()):
+        from decode_attention_amd.build import build
+        build()
+    return da.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_api():
+    assert declared_functions() == sorted(B.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5):
+        s = da.attn_status_string(code)
+        assert s and s != "unknown status"
+    assert da.attn_status_string(-99) == "unknown status"
+
+
+def _shape(**kw):
+    base = dict(batch=4, num_kv_heads=8, group=2, head_dim=256, max_pages_per_seq=8, num_pages=32,
+                kv_dtype=B.DA_DTYPE_BF16)
+    base.update(kw)
+    return B.make_shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation rejects first
+NULL = ctypes.c_void_p(0)
+
+
+def sliding(lib, shape, window=1024, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return lib.attn_decode_sliding(p[0], p[1], p[2], p[3], p[4], window, p[5], ctypes.byref(shape)
+                                   if shape is not None else None, NULL)
+
+
+def test_sliding_validation(lib):
+    assert sliding(lib, None) == -1
+    assert sliding(lib, _shape(), window=-1) == -1
+    assert sliding(lib, _shape(batch=0)) == -1
+    assert sliding(lib, _shape(num_pages=0)) == -1
+    assert sliding(lib, _shape(kv_dtype=7)) == -1
+    assert sliding(lib, _shape(), ptrs=[FAKE, FAKE, NULL, FAKE, FAKE, FAKE]) == -1
+    assert sliding(lib, _shape(head_dim=128)) == -2
+    assert sliding(lib, _shape(group=4)) == -2
+    s = _shape()
+    s.page_size = 32
+    assert sliding(lib, s) == -2
+    s = _shape()
+    s.out_dtype = B.DA_DTYPE_BF16
+    assert sliding(lib, s) == -2
+
+
+def _gshape(**kw):
+    base = dict(batch=4, num_kv_heads=1, group=16, head_dim=512, max_pages_per_seq=8, num_pages=32,
+                kv_dtype=B.DA_DTYPE_BF16)
+    base.update(kw)
+    return B.make_shape(**base)
+
+
+def glob(lib, shape, ws=FAKE, ws_bytes=1 << 30, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return lib.attn_decode_global(p[0], p[1], p[2], p[3], p[4], ctypes.byref(shape), ws, ws_bytes, NULL)
+
+
+def test_global_validation(lib):
+    assert glob(lib, _gshape(batch=-1)) == -1
+    assert glob(lib, _gshape(), ptrs=[FAKE, NULL, FAKE, FAKE, FAKE]) == -1
+    assert glob(lib, _gshape(group=8)) == -2
+    assert glob(lib, _gshape(kv_dtype=B.DA_DTYPE_F32)) == -2
+    assert glob(lib, _gshape(batch=5000)) == -2
+
+
+def test_workspace_bytes_with_explicit_splits(lib):
+    assert da.attn_decode_global_workspace_bytes(_gshape(num_splits=1)) == 0
+    n = da.attn_decode_global_workspace_bytes(_gshape(num_splits=10))
+    assert n == 16384 + 2 * 10 * (16 * 512 + 32) * 4
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_no_device_reported_after_valid_arguments(lib):
+    assert sliding(lib, _shape()) == -4
+    assert glob(lib, _gshape()) == -4
+    n = ctypes.c_size_t(0)
+    assert lib.attn_decode_global_workspace_bytes(ctypes.byref(_gshape()), ctypes.byref(n)) == -4

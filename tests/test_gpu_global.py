@@ -1,0 +1,87 @@
+"""GPU parity of attn_decode_global (values = keys, split over workgroups with
+the log-sum-exp merge) against the fp64 oracle, through the C ABI.
+
+Bar: max-abs 2e-2 for bf16 KV (fp32 accumulate, fp32 out).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from decode_attention_amd import inputs as I
+
+from gpu_util import BF16_TOL, global_on_gpu, max_abs
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_rows(wl, rows):
+    sub_q = wl.q[rows]
+    return oracle.paged_decode_global(sub_q, wl.kv_cache, wl.block_table[rows], wl.seq_lens[rows],
+                                      wl.kv_dtype)
+
+
+def check(wl, label, num_splits=0, rows=None):
+    print(f"[global] {label}: B={len(wl.seq_lens)} splits={num_splits}", flush=True)
+    got = global_on_gpu(wl, num_splits)
+    rows = np.arange(len(wl.seq_lens)) if rows is None else np.asarray(rows)
+    ref = oracle_rows(wl, rows)
+    err = max_abs(got[rows], ref)
+    print(f"[global] {label}: max-abs error {err:.3e} over {len(rows)} sequences", flush=True)
+    assert np.isfinite(got).all(), label
+    assert err <= BF16_TOL, (label, err)
+    return got, ref
+
+
+SMALL = [0, 1, 2, 15, 16, 17, 100, 1000, 4097, 333]
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 64, 1000])
+def test_ragged_lengths_every_split(gpu_lib, num_splits):
+    wl = I.make_global(SMALL, kv_dtype="bf16", tag=(400,), **I.GLOBAL)
+    got, _ = check(wl, "ragged", num_splits)
+    assert np.all(got[0] == 0)
+
+
+def test_split_invariance(gpu_lib):
+    wl = I.make_global([5000, 1, 20000, 7777], kv_dtype="bf16", tag=(401,), **I.GLOBAL)
+    outs = [global_on_gpu(wl, s) for s in (1, 2, 5, 37, 256, 0)]
+    # The weights reach the MFMAs as bf16 hi + lo parts (about 2^-17 relative),
+    # so splits differ only by that and by fp32 summation order.
+    for o in outs[1:]:
+        assert max_abs(o, outs[0]) <= 2e-4
+    ref = oracle_rows(wl, np.arange(4))
+    assert max_abs(outs[0], ref) <= BF16_TOL
+
+
+def test_single_token_returns_its_row(gpu_lib):
+    wl = I.make_global([1, 1, 1], kv_dtype="bf16", tag=(402,), **I.GLOBAL)
+    got = global_on_gpu(wl)
+    for b in range(3):
+        k = oracle.gather_tiled_cache(wl.kv_cache, wl.block_table[b], [0])[0, 0]
+        kf = oracle.stored_to_f64(k, "bf16")
+        np.testing.assert_array_equal(got[b], np.broadcast_to(kf, (16, 512)))
+
+
+@pytest.mark.parametrize("mode", ["q_zero", "q_small"])
+def test_diffuse_softmax(gpu_lib, mode):
+    kw = dict(q_zero=True) if mode == "q_zero" else dict(q_scale=1 / 22.6)
+    wl = I.make_global([1, 300, 5000], kv_dtype="bf16", tag=(403,), **I.GLOBAL, **kw)
+    check(wl, mode)
+
+
+def test_deterministic(gpu_lib):
+    wl = I.make_global([10000, 3, 777], kv_dtype="bf16", tag=(404,), **I.GLOBAL)
+    assert np.array_equal(global_on_gpu(wl), global_on_gpu(wl))
+
+
+def test_config2_full_size_sampled(gpu_lib):
+    wl = I.config_workload(2)
+    order = np.argsort(wl.seq_lens)
+    rows = np.unique(np.concatenate([order[:3], order[-3:], [0, 31, 63]]))
+    check(wl, "config 2", rows=rows)
+
+
+def test_config3_long_context(gpu_lib):
+    wl = I.config_workload(3)
+    check(wl, "config 3")
