@@ -41,15 +41,15 @@ constexpr int kGPageElems = kPage * kGD;      // bf16 elements per page (8192)
 constexpr int kGSlotFloats = kGH * kGD + 2 * kGH;  // acc[16][512], m[16], l[16]
 constexpr int kGMaxBatch = 1024;
 constexpr float kGRescale = 32.f;  // lazy-rescale threshold, log2 units
-constexpr int kGIdChunk = 4 * kWave;  // page ids gathered per refill (4 per lane)
+constexpr int kGIdChunk = 4 * kWave;  // page ids gathered per refill (4 per lane); even
 // Workspace: a header with the page prefix table (written by workgroup 0 of
 // the decode kernel, read by the merge), then 2*G partial-result slots.
 constexpr size_t kGHeaderBytes = 16384;  // >= (2*kGMaxBatch + 1) ints
 static_assert((2 * kGMaxBatch + 1) * sizeof(int) <= kGHeaderBytes, "header too small");
 #ifndef DA_GLOBAL_RING
-#define DA_GLOBAL_RING 4
+#define DA_GLOBAL_RING 3
 #endif
-constexpr int kGBuf = DA_GLOBAL_RING;  // page slices held per wave (ring; kGBuf-1 in flight ahead)
+constexpr int kGBuf = DA_GLOBAL_RING;  // two-page steps held per wave (ring; kGBuf-1 ahead)
 
 struct GlobalArgs {
   const uint16_t* q;         // [B][16][512] bf16 bits
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
   __shared__ int s_tmp[kGThreads];
-  __shared__ f32x4 s_part[2][kGWaves][kWave];            // partial S^T tiles
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][kGSlice * kPage];  // V slices
+  __shared__ f32x4 s_part[2][kGWaves][2][kWave];  // partial S^T tiles, 2 pages
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][2][kGSlice * kPage];  // V slices
 
   build_prefix(a, s_pre, s_len, s_tmp);
   const int N = s_pre[a.B];
@@ -133,20 +133,27 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
   // holds the id of page c0 + 64q + i, so no block-table read sits on the
   // path of a page load.
   int ids[4] = {0, 0, 0, 0};
-  uint4 buf[kGBuf][kGKSteps];
+  // ring of kGBuf steps; a step is 2 consecutive pages of the range
+  uint4 buf[kGBuf][2][kGKSteps];
   const size_t lane_off = (size_t)wv * kGKSteps * 512 + (size_t)lane * 8;
-  auto issue = [&](int slot, int kk) {  // kk: page index inside the current chunk
+  auto page_id = [&](int kk) {  // kk: page index inside the current chunk
     const int r = kk & (kWave - 1), q = kk >> 6;
     const int i0 = __builtin_amdgcn_readlane(ids[0], r), i1 = __builtin_amdgcn_readlane(ids[1], r);
     const int i2 = __builtin_amdgcn_readlane(ids[2], r), i3 = __builtin_amdgcn_readlane(ids[3], r);
-    const int phys = q == 0 ? i0 : q == 1 ? i1 : q == 2 ? i2 : i3;
-    const size_t base = (size_t)phys * kGPageElems + lane_off;
+    return q == 0 ? i0 : q == 1 ? i1 : q == 2 ? i2 : i3;
+  };
+  auto issue = [&](int slot, int kk, int cn) {  // pages kk, kk+1 (clamped to the chunk)
 #pragma unroll
-    for (int i = 0; i < kGKSteps; ++i) buf[slot][i] = ld16(a.kv + base + (size_t)i * 512);
+    for (int h = 0; h < 2; ++h) {
+      const size_t base = (size_t)page_id(min(kk + h, cn - 1)) * kGPageElems + lane_off;
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i) buf[slot][h][i] = ld16(a.kv + base + (size_t)i * 512);
+    }
   };
 
-  // ---- compute state
-  int b_cur = -1;
+  // ---- compute state; b_beg/b_end/b_len cache s_pre[b], s_pre[b+1] and
+  // s_len[b] of the current sequence, so steps read no LDS for them.
+  int b_cur = -1, b_beg = 0, b_end = 0, b_len = 0;
   int seg_start = r0;
   uint4 qreg[kGKSteps];
   float m_run = -INFINITY, l_run = 0.f;
@@ -154,16 +161,22 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
 #pragma unroll
   for (int t = 0; t < kGMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // transposed-read byte offsets inside this wave's V slice, per m-tile
+  // transposed-read byte offset inside a V slice (m-tile t adds 512 t)
   const int s16 = lane & 15;
   const int tr_tok = 4 * g + (s16 >> 2);
   const int tr_off = ((s16 & 3) >> 1) * 256 + tr_tok * 16 + (s16 & 1) * 8;
-  uint16_t* vs = s_v[wv];
+
+  auto load_q = [&](int b) {
+    const uint16_t* qb = a.q + ((size_t)b * kGH + hq) * kGD + wv * kGSlice + 8 * g;
+#pragma unroll
+    for (int i = 0; i < kGKSteps; ++i) qreg[i] = ld16(qb + 32 * i);
+    wait_vmem_all();
+  };
 
   auto finish_segment = [&](int b, int seg_end) {
     float lt = l_run + xor16(l_run);
     lt += xor32(lt);
-    const bool whole = (seg_start == s_pre[b]) && (seg_end == s_pre[b + 1]);
+    const bool whole = (seg_start == b_beg) && (seg_end == b_end);
     float* dst;
     float scale;
     if (whole) {
@@ -191,57 +204,80 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
     seg_start = seg_end;
   };
 
-  auto compute = [&](int slot, int p, int it) {
-    // sequence of page p (uniform); reload q at a sequence change
-    if (b_cur < 0 || s_pre[b_cur + 1] <= p) {
-      b_cur = (b_cur < 0) ? seq_of_page(s_pre, a.B, p) : b_cur;
-      while (s_pre[b_cur + 1] <= p) ++b_cur;
-      const uint16_t* qb = a.q + ((size_t)b_cur * kGH + hq) * kGD + wv * kGSlice + 8 * g;
+  // One step over the two pages of ring slot `slot` for sequence b. Page h
+  // (0 or 1) takes part iff use[h]; j[h] is its page index in the sequence.
+  // Tokens past the end of the sequence, and pages that do not take part,
+  // get weight 0 and a zeroed V (0 * NaN would poison the MFMA sums).
+  // s_part is double-buffered by exchange: consecutive steps must alternate
+  // buffers (one barrier separates a buffer's reads from its next writes).
+  int xb = 0;
+  auto step = [&](int slot, int jA, bool useA, int jB, bool useB) {
+    const int L = b_len;
+    const int it = xb;
+    xb ^= 1;
+    const int jj[2] = {jA, jB};
+    const bool use[2] = {useA, useB};
+    f32x4 sp[2];
 #pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) qreg[i] = ld16(qb + 32 * i);
-      wait_vmem_all();
+    for (int h = 0; h < 2; ++h) {
+      sp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i)
+        sp[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[slot][h][i]),
+                                                        __builtin_bit_cast(bf16x8, qreg[i]), sp[h], 0, 0, 0);
+      s_part[it & 1][wv][h][lane] = sp[h];
     }
-    const int b = b_cur;
-    const int j = p - s_pre[b];
-    const int L = s_len[b];
-    const bool last_page = (j + 1) * kPage > L;
-
-    // partial S^T over this wave's 128 coordinates
-    f32x4 sp = {0.f, 0.f, 0.f, 0.f};
+    // Edge step: a page left out, or tokens past the sequence end. Rare, so
+    // the common path carries no masking work.
+    const bool edge = !useA || !useB || (jB + 1) * kPage > L;
 #pragma unroll
-    for (int i = 0; i < kGKSteps; ++i)
-      sp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[slot][i]),
-                                                   __builtin_bit_cast(bf16x8, qreg[i]), sp, 0, 0, 0);
-    s_part[it & 1][wv][lane] = sp;
-    // V slice: zero tokens past the end of the sequence (0 * NaN = NaN)
-    if (last_page && j * kPage + (lane & 15) >= L) {
+    for (int h = 0; h < 2; ++h) {
+      uint16_t* vs = s_v[wv][h];
 #pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) buf[slot][i] = make_uint4(0u, 0u, 0u, 0u);
+      for (int i = 0; i < kGKSteps; ++i)
+        *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[slot][h][i];
     }
+    if (edge) {  // zero the V rows of tokens with weight 0 (this lane's token)
 #pragma unroll
-    for (int i = 0; i < kGKSteps; ++i)
-      *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[slot][i];
+      for (int h = 0; h < 2; ++h) {
+        if (!(use[h] && jj[h] * kPage + (lane & 15) < L)) {
+          uint16_t* vs = s_v[wv][h];
+#pragma unroll
+          for (int i = 0; i < kGKSteps; ++i)
+            *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
     __syncthreads();
-    f32x4 s = s_part[it & 1][0][lane];
+    float sc[8];
 #pragma unroll
-    for (int ww = 1; ww < kGWaves; ++ww) s += s_part[it & 1][ww][lane];
-
-    float sc[4];
+    for (int h = 0; h < 2; ++h) {
+      f32x4 s = s_part[it & 1][0][h][lane];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sc[e] = s[e] * kLog2e;
-      if (last_page && j * kPage + 4 * g + e >= L) sc[e] = -INFINITY;
+      for (int ww = 1; ww < kGWaves; ++ww) s += s_part[it & 1][ww][h][lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[4 * h + e] = s[e] * kLog2e;
     }
-    float mp = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mp = fmaxf(mp, xor16(mp));
-    mp = fmaxf(mp, xor32(mp));
+    if (edge) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (!(use[h] && jj[h] * kPage + 4 * g + e < L)) sc[4 * h + e] = -INFINITY;
+    }
     // Lazy rescaling: m_run is a reference, not the exact running max. It
-    // moves (and the state is rescaled) only when a head's page max exceeds
-    // it by more than kGRescale (log2 units), so p = 2^(s - m_run) stays
-    // below 2^kGRescale and no fp32 quantity can overflow; any reference
-    // gives the same softmax since numerator and denominator share it.
-    // Always taken on a segment's first page (m_run = -inf).
-    if (__any(mp > m_run + kGRescale)) {
+    // moves (and the state is rescaled) only when a score exceeds it by more
+    // than kGRescale (log2 units), so p = 2^(s - m_run) stays below
+    // 2^kGRescale and no fp32 quantity can overflow; any reference gives the
+    // same softmax since numerator and denominator share it. The common case
+    // needs no cross-lane max at all. Always taken on a segment's first step
+    // (m_run = -inf).
+    float lmax = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sc[e]);
+    if (__any(lmax > m_run + kGRescale)) {
+      float mp = fmaxf(lmax, xor16(lmax));
+      mp = fmaxf(mp, xor32(mp));                                   // head max
       const float m_new = (mp > m_run + kGRescale) ? mp : m_run;  // mp finite
       const float alpha = exp2_fast(m_run - m_new);                // 0 from -inf
       m_run = m_new;
@@ -249,36 +285,70 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
 #pragma unroll
       for (int t = 0; t < kGMTiles; ++t) acc[t] *= alpha;
     }
-    const float m_new = m_run;
     // p = p_hi + p_lo with both parts in bf16: the two MFMAs below carry p
     // to about 2^-17 relative, so the result does not depend on where the
     // reference (and hence the bf16 rounding of p) happened to be.
-    bf16x4 ph, pl;
+    bf16x8 ph, pl;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = exp2_fast(sc[e] - m_new);
-      ph[e] = (__bf16)p;
-      pl[e] = (__bf16)(p - (float)ph[e]);
-      l_run += p;
+    for (int e = 0; e < 8; ++e) {
+      const float pv = exp2_fast(sc[e] - m_run);
+      ph[e] = (__bf16)pv;
+      pl[e] = (__bf16)(pv - (float)ph[e]);
+      l_run += pv;
     }
+    // O^T (d x heads) += V^T P^T over the 32 tokens of the step:
+    // k-slots 8g..8g+3 are page A's tokens 4g..4g+3, 8g+4..8g+7 page B's.
 #pragma unroll
     for (int t = 0; t < kGMTiles; ++t) {
-      const bf16x4 vt = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)vs +
-                                                     t * 512 + tr_off)));
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, ph, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pl, acc[t], 0, 0, 0);
+      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)s_v[wv][0] +
+                                                     t * 512 + tr_off));
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)s_v[wv][1] +
+                                                     t * 512 + tr_off));
+      const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, ph, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pl, acc[t], 0, 0, 0);
     }
-    const int seg_end = min(r1, s_pre[b + 1]);
-    if (p + 1 == seg_end) finish_segment(b, seg_end);
   };
 
-  // Ring of kGBuf page slices, kGBuf-1 pages ahead. Prefetches past the
-  // chunk's end are clamped to its last page (redundant, cache-resident
-  // loads) so that every pass issues the same loads.
-  int it = 0;
+  // Sequence of page p (uniform); reloads q when the sequence changes.
+  auto enter = [&](int p) {
+    if (p >= b_end) {  // also true before the first page (b_end = 0)
+      b_cur = (b_cur < 0) ? seq_of_page(s_pre, a.B, p) : b_cur;
+      while (s_pre[b_cur + 1] <= p) ++b_cur;
+      b_beg = __builtin_amdgcn_readfirstlane(s_pre[b_cur]);
+      b_end = __builtin_amdgcn_readfirstlane(s_pre[b_cur + 1]);
+      b_len = __builtin_amdgcn_readfirstlane(s_len[b_cur]);
+      load_q(b_cur);
+    }
+    return b_cur;
+  };
+
+  // Steps of two pages in range order. A step whose second page starts a new
+  // sequence is done twice, once per page, with the other page left out.
+  auto run_step = [&](int slot, int c0, int kk, int cn) {
+    const int pA = c0 + kk, pB = pA + 1;
+    const bool hasB = pB < r1 && kk + 1 < cn;
+    // pass 0: page A (and B if it is in A's segment); pass 1: page B alone
+    for (int pass = 0; pass < 2; ++pass) {
+      const int pf = pass == 0 ? pA : pB;     // first page of this pass
+      const int b = enter(pf);
+      const int end = min(r1, b_end);  // end of the segment
+      const bool useA = pass == 0;
+      const bool useB = hasB && (pass == 1 || pB < end);
+      step(slot, pA - b_beg, useA, pB - b_beg, useB);
+      const int last = useB ? pB : pA;
+      if (last + 1 == end) finish_segment(b, end);
+      if (useB || !hasB) break;  // nothing left for a second pass
+    }
+  };
+
+  // Ring of kGBuf steps, kGBuf-1 steps ahead. Loads past the chunk's end are
+  // clamped to its last page (redundant, cache-resident) so that every pass
+  // issues the same loads and the compiler waits only for the slot in use.
   for (int c0 = r0; c0 < r1; c0 += kGIdChunk) {
-    const int cn = min(r1 - c0, kGIdChunk);
+    const int cn = min(r1 - c0, kGIdChunk);   // even except at the range's end
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int p = c0 + q * kWave + lane;
@@ -291,19 +361,13 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
     }
     wait_vmem_all();
 #pragma unroll
-    for (int u = 0; u < kGBuf - 1; ++u) issue(u, min(u, cn - 1));
-    for (int base = 0; base < cn; base += kGBuf) {
-      // No early exit: every step issues one page, so the compiler sees the
-      // same number of loads in flight on every path and waits only for the
-      // slot being computed.
+    for (int u = 0; u < kGBuf - 1; ++u) issue(u, min(2 * u, cn - 1), cn);
+    for (int base = 0; base < cn; base += 2 * kGBuf) {
 #pragma unroll
       for (int u = 0; u < kGBuf; ++u) {
-        const int kk = base + u;
-        issue((u + kGBuf - 1) % kGBuf, min(kk + kGBuf - 1, cn - 1));
-        if (kk < cn) {
-          compute(u, c0 + kk, it);
-          ++it;
-        }
+        const int kk = base + 2 * u;
+        issue((u + kGBuf - 1) % kGBuf, min(kk + 2 * (kGBuf - 1), cn - 1), cn);
+        if (kk < cn) run_step(u, c0, kk, cn);
       }
     }
   }

@@ -43,6 +43,16 @@ def test_ragged_lengths_every_split(gpu_lib, num_splits):
     assert np.all(got[0] == 0)
 
 
+@pytest.mark.parametrize("num_splits", [0, 1, 3, 17, 100])
+def test_many_short_sequences(gpu_lib, num_splits):
+    # 1-3 pages per sequence: two-page steps often straddle a sequence start,
+    # and workgroup ranges cut sequences at odd page offsets.
+    rng = np.random.default_rng(405)
+    lens = rng.integers(1, 48, size=200)
+    wl = I.make_global(lens, kv_dtype="bf16", tag=(405,), **I.GLOBAL)
+    check(wl, f"short sequences, splits {num_splits}", num_splits)
+
+
 def test_split_invariance(gpu_lib):
     wl = I.make_global([5000, 1, 20000, 7777], kv_dtype="bf16", tag=(401,), **I.GLOBAL)
     outs = [global_on_gpu(wl, s) for s in (1, 2, 5, 37, 256, 0)]
