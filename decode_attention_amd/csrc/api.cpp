@@ -12,7 +12,7 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kGlobalMaxBatch = 1024;   // per-call prefix table held in LDS
+constexpr int kGlobalMaxBatch = 256;    // per-call prefix table held in LDS (model domain B <= 256)
 constexpr int kGlobalMaxSplits = 1 << 16;
 
 struct DeviceInfo {

@@ -13,18 +13,25 @@
 // (scores are kept in the log2 domain). This is exact over the reals because
 // the softmax over a union of disjoint key sets factorises that way.
 //
-// Inside a workgroup the 4 waves share every page: wave w owns coordinates
-// [128w, 128w+128), i.e. 4 KB of the 16 KB page, loaded with lane-linear
+// A workgroup (one per compute unit) has 8 waves in 4 pairs. The pairs take
+// the pages of a segment round-robin, 4 pages per step, and all 8 waves meet
+// at one barrier per step, so no wave on the compute unit runs ahead of the
+// others; the 4 pair states are merged through LDS when the segment ends.
+// Inside a pair the 2 waves share a page: wave half h owns coordinates
+// [256h, 256h+256), i.e. 8 KB of the 16 KB page, loaded with lane-linear
 // 16-byte loads that land directly in the MFMA A-operand layout of K.
-//   S^T (16 tokens x 16 heads) = K Q^T : 4 x mfma_f32_16x16x32_bf16 per wave
-//     on its 128 coordinates; the 4 partial tiles are summed through LDS in a
-//     fixed order, so every wave holds the same scores.
+//   S^T (16 tokens x 16 heads) = K Q^T : 8 x mfma_f32_16x16x32_bf16 per wave
+//     on its 256 coordinates; the 2 partial tiles are added through LDS in a
+//     fixed order, so both waves hold the same scores.
 //   The S^T accumulator layout (lane: head l%16, tokens 4(l/16)..+3) is the
-//     B operand of mfma_f32_16x16x16_bf16 for P^T, so the probabilities never
-//     move between lanes.
-//   O^T (512 x 16) += V^T P^T: V = K, the wave's 4 KB is written to LDS once
-//     and read back transposed with ds_read_b64_tr_b16 (each instruction
-//     covers 512 contiguous bytes, no bank conflicts).
+//     B operand layout of the PV product, so probabilities never move
+//     between lanes.
+//   O^T (256 x 16 per wave) += V^T P^T: V = K, the wave's 8 KB is written to
+//     LDS once and read back transposed with ds_read_b64_tr_b16 (512
+//     contiguous bytes per instruction). One mfma_f32_16x16x32_bf16 per
+//     16-row tile: its 32-wide k dimension holds the page's 16 tokens twice,
+//     against bf16(p) and against bf16(p - bf16(p)), so p enters the product
+//     to about 2^-17 relative.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,14 +39,19 @@ namespace da {
 
 constexpr int kGD = 512;          // head dim
 constexpr int kGH = 16;           // query heads (KV head count 1)
-constexpr int kGWaves = 4;        // waves per workgroup
+constexpr int kGPair = 2;         // waves sharing a page (coordinate halves)
+constexpr int kGPairs = 4;        // pairs per workgroup (4 pages per step)
+constexpr int kGWaves = kGPair * kGPairs;
 constexpr int kGThreads = kGWaves * kWave;
-constexpr int kGSlice = kGD / kGWaves;        // coordinates per wave (128)
-constexpr int kGKSteps = kGSlice / 32;        // 16x16x32 k-steps per wave (4)
-constexpr int kGMTiles = kGSlice / 16;        // 16-row output tiles per wave (8)
+constexpr int kGSlice = kGD / kGPair;         // coordinates per wave (256)
+constexpr int kGKSteps = kGSlice / 32;        // 16x16x32 k-steps per wave (8)
+constexpr int kGMTiles = kGSlice / 16;        // 16-row output tiles per wave (16)
 constexpr int kGPageElems = kPage * kGD;      // bf16 elements per page (8192)
-constexpr int kGSlotFloats = kGH * kGD + 2 * kGH;  // acc[16][512], m[16], l[16]
-constexpr int kGMaxBatch = 1024;
+// Partial slot: the unnormalised output in lane order, [2 halves][16 tiles]
+// [64 lanes][4] floats (element (h, d) with d = 256f + 16t + 4g + e sits at
+// lane h + 16g, tile t, half f), then m[16] and l[16].
+constexpr int kGSlotFloats = kGH * kGD + 2 * kGH;
+constexpr int kGMaxBatch = 256;   // the model's batch domain is [1, 256]
 constexpr float kGRescale = 32.f;  // lazy-rescale threshold, log2 units
 constexpr int kGIdChunk = 4 * kWave;  // page ids gathered per refill (4 per lane); even
 // Workspace: a header with the page prefix table (written by workgroup 0 of
@@ -49,7 +61,7 @@ static_assert((2 * kGMaxBatch + 1) * sizeof(int) <= kGHeaderBytes, "header too s
 #ifndef DA_GLOBAL_RING
 #define DA_GLOBAL_RING 3
 #endif
-constexpr int kGBuf = DA_GLOBAL_RING;  // two-page steps held per wave (ring; kGBuf-1 ahead)
+constexpr int kGBuf = DA_GLOBAL_RING;  // pages held per wave (ring; kGBuf-1 ahead)
 
 struct GlobalArgs {
   const uint16_t* q;         // [B][16][512] bf16 bits
@@ -106,12 +118,14 @@ __device__ __forceinline__ int seq_of_page(const int* s_pre, int B, int p) {
   return lo;
 }
 
-__global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) {
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) void global_decode_kernel(GlobalArgs a) {
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
   __shared__ int s_tmp[kGThreads];
-  __shared__ f32x4 s_part[2][kGWaves][2][kWave];  // partial S^T tiles, 2 pages
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][2][kGSlice * kPage];  // V slices
+  __shared__ f32x4 s_part[2][kGWaves][kWave];  // partial S^T tiles (double-buffered)
+  // V slices, one per wave; also the merge area at the end of a segment
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][kGSlice * kPage];
+  __shared__ float s_ml[4][2][kWave];           // m, l of the wave states being merged
 
   build_prefix(a, s_pre, s_len, s_tmp);
   const int N = s_pre[a.B];
@@ -126,155 +140,73 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int pr = wv >> 1;          // pair
+  const int hf = wv & 1;           // coordinate half of this wave
   const int hq = lane & 15;        // head of this lane's S^T / O^T column
   const int g = lane >> 4;         // token quad of this lane (S^T rows 4g..4g+3)
 
-  // ---- physical page ids of the range, 256 at a time: lane i of ids[q]
-  // holds the id of page c0 + 64q + i, so no block-table read sits on the
-  // path of a page load.
-  int ids[4] = {0, 0, 0, 0};
-  // ring of kGBuf steps; a step is 2 consecutive pages of the range
-  uint4 buf[kGBuf][2][kGKSteps];
-  const size_t lane_off = (size_t)wv * kGKSteps * 512 + (size_t)lane * 8;
-  auto page_id = [&](int kk) {  // kk: page index inside the current chunk
+  int ids[4] = {0, 0, 0, 0};       // physical ids of this pair's pages, 256 at a time
+  uint4 buf[kGBuf][kGKSteps];      // ring of this wave's page slices
+  uint4 qreg[kGKSteps];            // Q^T B operands: head hq, d = 256hf + 32i + 8g .. +8
+  f32x4 acc[kGMTiles];             // O^T: head hq, d = 256hf + 16t + 4g + e
+  float m_run = -INFINITY, l_run = 0.f;
+  const size_t lane_off = (size_t)hf * kGKSteps * 512 + (size_t)lane * 8;
+  uint16_t* vs = s_v[wv];
+  const int s16 = lane & 15;
+  const int tr_tok = 4 * g + (s16 >> 2);
+  const int tr_off = ((s16 & 3) >> 1) * 256 + tr_tok * 16 + (s16 & 1) * 8;  // + 512 t
+
+  auto issue = [&](int slot, int kk) {  // kk: step index inside the current id chunk
     const int r = kk & (kWave - 1), q = kk >> 6;
     const int i0 = __builtin_amdgcn_readlane(ids[0], r), i1 = __builtin_amdgcn_readlane(ids[1], r);
     const int i2 = __builtin_amdgcn_readlane(ids[2], r), i3 = __builtin_amdgcn_readlane(ids[3], r);
-    return q == 0 ? i0 : q == 1 ? i1 : q == 2 ? i2 : i3;
-  };
-  auto issue = [&](int slot, int kk, int cn) {  // pages kk, kk+1 (clamped to the chunk)
+    const int phys = q == 0 ? i0 : q == 1 ? i1 : q == 2 ? i2 : i3;
+    const size_t base = (size_t)phys * kGPageElems + lane_off;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const size_t base = (size_t)page_id(min(kk + h, cn - 1)) * kGPageElems + lane_off;
-#pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) buf[slot][h][i] = ld16(a.kv + base + (size_t)i * 512);
-    }
+    for (int i = 0; i < kGKSteps; ++i) buf[slot][i] = ld16(a.kv + base + (size_t)i * 512);
   };
 
-  // ---- compute state; b_beg/b_end/b_len cache s_pre[b], s_pre[b+1] and
-  // s_len[b] of the current sequence, so steps read no LDS for them.
-  int b_cur = -1, b_beg = 0, b_end = 0, b_len = 0;
-  int seg_start = r0;
-  uint4 qreg[kGKSteps];
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 acc[kGMTiles];
-#pragma unroll
-  for (int t = 0; t < kGMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // transposed-read byte offset inside a V slice (m-tile t adds 512 t)
-  const int s16 = lane & 15;
-  const int tr_tok = 4 * g + (s16 >> 2);
-  const int tr_off = ((s16 & 3) >> 1) * 256 + tr_tok * 16 + (s16 & 1) * 8;
-
-  auto load_q = [&](int b) {
-    const uint16_t* qb = a.q + ((size_t)b * kGH + hq) * kGD + wv * kGSlice + 8 * g;
-#pragma unroll
-    for (int i = 0; i < kGKSteps; ++i) qreg[i] = ld16(qb + 32 * i);
-    wait_vmem_all();
-  };
-
-  auto finish_segment = [&](int b, int seg_end) {
-    float lt = l_run + xor16(l_run);
-    lt += xor32(lt);
-    const bool whole = (seg_start == b_beg) && (seg_end == b_end);
-    float* dst;
-    float scale;
-    if (whole) {
-      dst = a.out + (size_t)b * kGH * kGD;
-      scale = 1.f / lt;
-    } else {
-      const int slot = 2 * w + (seg_start == r0 ? 0 : 1);
-      float* ws = a.ws + (size_t)slot * kGSlotFloats;
-      dst = ws;
-      scale = 1.f;
-      if (wv == 0 && g == 0) {
-        ws[kGH * kGD + hq] = m_run;
-        ws[kGH * kGD + kGH + hq] = lt;
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kGMTiles; ++t) {
-      const int d = wv * kGSlice + t * 16 + 4 * g;
-      f32x4 v = acc[t] * scale;
-      *reinterpret_cast<f32x4*>(dst + (size_t)hq * kGD + d) = v;
-      acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    m_run = -INFINITY;
-    l_run = 0.f;
-    seg_start = seg_end;
-  };
-
-  // One step over the two pages of ring slot `slot` for sequence b. Page h
-  // (0 or 1) takes part iff use[h]; j[h] is its page index in the sequence.
-  // Tokens past the end of the sequence, and pages that do not take part,
-  // get weight 0 and a zeroed V (0 * NaN would poison the MFMA sums).
-  // s_part is double-buffered by exchange: consecutive steps must alternate
-  // buffers (one barrier separates a buffer's reads from its next writes).
+  // s_part is double-buffered by step: consecutive steps alternate buffers
+  // (one barrier separates a buffer's reads from its next writes).
   int xb = 0;
-  auto step = [&](int slot, int jA, bool useA, int jB, bool useB) {
-    const int L = b_len;
-    const int it = xb;
-    xb ^= 1;
-    const int jj[2] = {jA, jB};
-    const bool use[2] = {useA, useB};
-    f32x4 sp[2];
+  // One step for this pair: page j of the current sequence (L cached tokens)
+  // from ring slot `slot`; `valid` false when the pair has no page this step.
+  auto compute = [&](int slot, int j, bool valid, int L) {
+    f32x4 s2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kGKSteps; ++i)
+      s2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[slot][i]),
+                                                          __builtin_bit_cast(bf16x8, qreg[i]), s2[i & 1],
+                                                          0, 0, 0);
+    s_part[xb][wv][lane] = s2[0] + s2[1];
 #pragma unroll
-      for (int i = 0; i < kGKSteps; ++i)
-        sp[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[slot][h][i]),
-                                                        __builtin_bit_cast(bf16x8, qreg[i]), sp[h], 0, 0, 0);
-      s_part[it & 1][wv][h][lane] = sp[h];
-    }
-    // Edge step: a page left out, or tokens past the sequence end. Rare, so
-    // the common path carries no masking work.
-    const bool edge = !useA || !useB || (jB + 1) * kPage > L;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      uint16_t* vs = s_v[wv][h];
+    for (int i = 0; i < kGKSteps; ++i) *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[slot][i];
+    const bool edge = !valid || (j + 1) * kPage > L;  // rare
+    if (edge && (!valid || j * kPage + (lane & 15) >= L)) {
+      // zero the V row of this lane's token (weight 0; 0 * NaN would poison)
 #pragma unroll
       for (int i = 0; i < kGKSteps; ++i)
-        *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[slot][h][i];
-    }
-    if (edge) {  // zero the V rows of tokens with weight 0 (this lane's token)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (!(use[h] && jj[h] * kPage + (lane & 15) < L)) {
-          uint16_t* vs = s_v[wv][h];
-#pragma unroll
-          for (int i = 0; i < kGKSteps; ++i)
-            *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
+        *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
-    float sc[8];
+    const f32x4 s = s_part[xb][wv & ~1][lane] + s_part[xb][wv | 1][lane];
+    xb ^= 1;
+    if (!valid) return;  // uniform per pair; no barrier follows in this step
+    float sc[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      f32x4 s = s_part[it & 1][0][h][lane];
-#pragma unroll
-      for (int ww = 1; ww < kGWaves; ++ww) s += s_part[it & 1][ww][h][lane];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[4 * h + e] = s[e] * kLog2e;
-    }
+    for (int e = 0; e < 4; ++e) sc[e] = s[e] * kLog2e;
     if (edge) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (!(use[h] && jj[h] * kPage + 4 * g + e < L)) sc[4 * h + e] = -INFINITY;
+      for (int e = 0; e < 4; ++e)
+        if (j * kPage + 4 * g + e >= L) sc[e] = -INFINITY;
     }
     // Lazy rescaling: m_run is a reference, not the exact running max. It
     // moves (and the state is rescaled) only when a score exceeds it by more
     // than kGRescale (log2 units), so p = 2^(s - m_run) stays below
     // 2^kGRescale and no fp32 quantity can overflow; any reference gives the
     // same softmax since numerator and denominator share it. The common case
-    // needs no cross-lane max at all. Always taken on a segment's first step
-    // (m_run = -inf).
-    float lmax = sc[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sc[e]);
+    // needs no cross-lane max. Always taken on a pair's first page.
+    const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
     if (__any(lmax > m_run + kGRescale)) {
       float mp = fmaxf(lmax, xor16(lmax));
       mp = fmaxf(mp, xor32(mp));                                   // head max
@@ -285,113 +217,141 @@ __global__ __launch_bounds__(kGThreads) void global_decode_kernel(GlobalArgs a) 
 #pragma unroll
       for (int t = 0; t < kGMTiles; ++t) acc[t] *= alpha;
     }
-    // p = p_hi + p_lo with both parts in bf16: the two MFMAs below carry p
-    // to about 2^-17 relative, so the result does not depend on where the
-    // reference (and hence the bf16 rounding of p) happened to be.
-    bf16x8 ph, pl;
+    // P^T operand: k-slots 8g..8g+3 hold bf16(p) of tokens 4g..4g+3 and
+    // 8g+4..8g+7 the remainder bf16(p - bf16(p)); the V^T operand repeats the
+    // same 4 tokens in both halves.
+    bf16x8 pp;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const float pv = exp2_fast(sc[e] - m_run);
-      ph[e] = (__bf16)pv;
-      pl[e] = (__bf16)(pv - (float)ph[e]);
+      pp[e] = (__bf16)pv;
+      pp[4 + e] = (__bf16)(pv - (float)pp[e]);
       l_run += pv;
     }
-    // O^T (d x heads) += V^T P^T over the 32 tokens of the step:
-    // k-slots 8g..8g+3 are page A's tokens 4g..4g+3, 8g+4..8g+7 page B's.
 #pragma unroll
     for (int t = 0; t < kGMTiles; ++t) {
-      const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)s_v[wv][0] +
+      const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)vs +
                                                      t * 512 + tr_off));
-      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)s_v[wv][1] +
-                                                     t * 512 + tr_off));
-      const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(va, vb, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, ph, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pl, acc[t], 0, 0, 0);
+      const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v4, v4, 0, 1, 2, 3, 0, 1, 2, 3));
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pp, acc[t], 0, 0, 0);
     }
   };
 
-  // Sequence of page p (uniform); reloads q when the sequence changes.
-  auto enter = [&](int p) {
-    if (p >= b_end) {  // also true before the first page (b_end = 0)
-      b_cur = (b_cur < 0) ? seq_of_page(s_pre, a.B, p) : b_cur;
-      while (s_pre[b_cur + 1] <= p) ++b_cur;
-      b_beg = __builtin_amdgcn_readfirstlane(s_pre[b_cur]);
-      b_end = __builtin_amdgcn_readfirstlane(s_pre[b_cur + 1]);
-      b_len = __builtin_amdgcn_readfirstlane(s_len[b_cur]);
-      load_q(b_cur);
-    }
-    return b_cur;
-  };
-
-  // Steps of two pages in range order. A step whose second page starts a new
-  // sequence is done twice, once per page, with the other page left out.
-  auto run_step = [&](int slot, int c0, int kk, int cn) {
-    const int pA = c0 + kk, pB = pA + 1;
-    const bool hasB = pB < r1 && kk + 1 < cn;
-    // pass 0: page A (and B if it is in A's segment); pass 1: page B alone
-    for (int pass = 0; pass < 2; ++pass) {
-      const int pf = pass == 0 ? pA : pB;     // first page of this pass
-      const int b = enter(pf);
-      const int end = min(r1, b_end);  // end of the segment
-      const bool useA = pass == 0;
-      const bool useB = hasB && (pass == 1 || pB < end);
-      step(slot, pA - b_beg, useA, pB - b_beg, useB);
-      const int last = useB ? pB : pA;
-      if (last + 1 == end) finish_segment(b, end);
-      if (useB || !hasB) break;  // nothing left for a second pass
-    }
-  };
-
-  // Ring of kGBuf steps, kGBuf-1 steps ahead. Loads past the chunk's end are
-  // clamped to its last page (redundant, cache-resident) so that every pass
-  // issues the same loads and the compiler waits only for the slot in use.
-  for (int c0 = r0; c0 < r1; c0 += kGIdChunk) {
-    const int cn = min(r1 - c0, kGIdChunk);   // even except at the range's end
+  // End-of-segment merge through LDS (the V regions are free by then): a
+  // wave state is m (per head), l (lane partial) and its 16 accumulator tiles.
+  f32x4* st = reinterpret_cast<f32x4*>(&s_v[0][0]);  // 4 states of [16][64] f32x4
+  auto put_state = [&](int k) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int p = c0 + q * kWave + lane;
-      int id = 0;
-      if (p < r1) {
-        const int bb = seq_of_page(s_pre, a.B, p);
-        id = a.bt[(size_t)bb * a.P_max + (p - s_pre[bb])];
+    for (int t = 0; t < kGMTiles; ++t) st[(k * kGMTiles + t) * kWave + lane] = acc[t];
+    s_ml[k][0][lane] = m_run;
+    s_ml[k][1][lane] = l_run;
+  };
+  auto take_state = [&](int k) {  // fold stored state k into this one
+    const float m_o = s_ml[k][0][lane], l_o = s_ml[k][1][lane];
+    const float M = fmaxf(m_run, m_o);
+    const float fs = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - M);
+    const float fo = (m_o == -INFINITY) ? 0.f : exp2_fast(m_o - M);
+#pragma unroll
+    for (int t = 0; t < kGMTiles; ++t) acc[t] = acc[t] * fs + st[(k * kGMTiles + t) * kWave + lane] * fo;
+    l_run = l_run * fs + l_o * fo;
+    m_run = M;
+  };
+
+  int b = seq_of_page(s_pre, a.B, r0);
+  for (int s0 = r0; s0 < r1;) {
+    while (s_pre[b + 1] <= s0) ++b;  // uniform; skips empty sequences
+    const int pb = __builtin_amdgcn_readfirstlane(s_pre[b]);
+    const int pe = __builtin_amdgcn_readfirstlane(s_pre[b + 1]);
+    const int L = __builtin_amdgcn_readfirstlane(s_len[b]);
+    const int s1 = min(r1, pe);                            // segment [s0, s1) of sequence b
+    const int nsteps = (s1 - s0 + kGPairs - 1) / kGPairs;  // this pair's page of step k: s0 + 4k + pr
+    {
+      const uint16_t* qb = a.q + ((size_t)b * kGH + hq) * kGD + hf * kGSlice + 8 * g;
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i) qreg[i] = ld16(qb + 32 * i);
+    }
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int t = 0; t < kGMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nsteps; c0 += kGIdChunk) {
+      const int cn = min(nsteps - c0, kGIdChunk);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = c0 + q * kWave + lane;
+        const int pg = s0 + kGPairs * k + pr;  // a step past the end loads the first page again
+        ids[q] = a.bt[(size_t)b * a.P_max + (k < nsteps && pg < s1 ? pg : s0) - pb];
       }
-      ids[q] = id;
-    }
-    wait_vmem_all();
+      wait_vmem_all();
+      // Ring of kGBuf steps, kGBuf-1 ahead; loads past the chunk's end are
+      // clamped to its last step (redundant, cache-resident) so that every
+      // pass issues the same loads and the compiler waits only for the slot
+      // in use.
 #pragma unroll
-    for (int u = 0; u < kGBuf - 1; ++u) issue(u, min(2 * u, cn - 1), cn);
-    for (int base = 0; base < cn; base += 2 * kGBuf) {
+      for (int u = 0; u < kGBuf - 1; ++u) issue(u, min(u, cn - 1));
+      for (int base = 0; base < cn; base += kGBuf) {
 #pragma unroll
-      for (int u = 0; u < kGBuf; ++u) {
-        const int kk = base + 2 * u;
-        issue((u + kGBuf - 1) % kGBuf, min(kk + 2 * (kGBuf - 1), cn - 1), cn);
-        if (kk < cn) run_step(u, c0, kk, cn);
+        for (int u = 0; u < kGBuf; ++u) {
+          const int kk = base + u;
+          issue((u + kGBuf - 1) % kGBuf, min(kk + kGBuf - 1, cn - 1));
+          if (kk < cn) {
+            const int pg = s0 + kGPairs * (c0 + kk) + pr;
+            compute(u, pg - pb, pg < s1, L);
+          }
+        }
       }
     }
+    // Merge the 4 pair states (same coordinate half): 2 -> 0 and 3 -> 1, then 1 -> 0.
+    __syncthreads();  // every wave is done with its V region
+    if (pr >= 2) put_state((pr - 2) * kGPair + hf);
+    __syncthreads();
+    if (pr < 2) take_state(pr * kGPair + hf);
+    __syncthreads();
+    if (pr == 1) put_state(hf);
+    __syncthreads();
+    if (pr == 0) {
+      take_state(hf);
+      float lt = l_run + xor16(l_run);
+      lt += xor32(lt);
+      if (s0 == pb && s1 == pe) {  // whole sequence in this workgroup: o[b][h][d]
+        float* dst = a.out + ((size_t)b * kGH + hq) * kGD + hf * kGSlice + 4 * g;
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int t = 0; t < kGMTiles; ++t) *reinterpret_cast<f32x4*>(dst + t * 16) = acc[t] * inv;
+      } else {                     // partial slot, lane order: 1 KB contiguous per store
+        float* ws = a.ws + (size_t)(2 * w + (s0 == r0 ? 0 : 1)) * kGSlotFloats;
+        if (hf == 0 && g == 0) {
+          ws[kGH * kGD + hq] = m_run;
+          ws[kGH * kGD + kGH + hq] = lt;
+        }
+#pragma unroll
+        for (int t = 0; t < kGMTiles; ++t)
+          *reinterpret_cast<f32x4*>(ws + ((size_t)(hf * kGMTiles + t) * kWave + lane) * 4) = acc[t];
+      }
+    }
+    __syncthreads();  // the merge area is page space again
+    s0 = s1;
   }
 }
 
 // Log-sum-exp merge of the partial results of split sequences. Workgroup:
-// (sequence b, head h, coordinate chunk of 4*TPS); its 256 threads form
-// 256/TPS slot groups of TPS threads, each thread one float4 of the chunk, so
-// the partials of a long sequence (hundreds of them) are read in parallel.
-// Each group folds its slots with a running max; the groups are then combined
-// the same way. The page prefix table comes from the workspace header.
-template <int TPS>
-__global__ __launch_bounds__(256) void lse_merge_kernel(GlobalArgs a) {
-  constexpr int NG = 256 / TPS;   // slot groups
-  constexpr int DCH = 4 * TPS;    // coordinates per workgroup
-  constexpr int NDC = kGD / DCH;  // chunks per head
-  __shared__ f32x4 s_num[NG][TPS];
-  __shared__ float s_m[NG], s_den[NG];
-  const int b = blockIdx.x / (kGH * NDC);
-  const int rem = blockIdx.x - b * (kGH * NDC);
-  const int h = rem / NDC;
-  const int tid = threadIdx.x;
-  const int grp = tid / TPS;
-  const int d0 = (rem - h * NDC) * DCH + (tid % TPS) * 4;
+// (sequence b, output tile T = 16 coordinates of all 16 heads, i.e. one
+// lane-order tile of a partial slot); its NG groups of 64 threads fold the
+// sequence's pieces w0+grp, w0+grp+NG, ... with a running max, reading 1 KB
+// contiguous per piece, and are then combined the same way. The page prefix
+// table comes from the workspace header.
+template <int NG>
+__global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
+  constexpr int kTiles = kGPair * kGMTiles;   // 32 tiles of 16 coordinates
+  __shared__ f32x4 s_num[NG][kWave];
+  __shared__ float s_m[NG][kWave], s_den[NG][kWave];
+  const int b = blockIdx.x / kTiles;
+  const int T = blockIdx.x - b * kTiles;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = threadIdx.x / kWave;
+  const int h = lane & 15, g = lane >> 4;
+  const int d0 = (T / kGMTiles) * kGSlice + (T % kGMTiles) * 16 + 4 * g;
   float* ob = a.out + ((size_t)b * kGH + h) * kGD + d0;
   const int* pre = a.ws_hdr;
   const int L = pre[a.B + 1 + b];
@@ -405,6 +365,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(GlobalArgs a) {
   auto wg_of = [&](int p) { return (int)((((long long)p + 1) * a.G - 1) / N); };
   const int w0 = wg_of(pb), w1 = wg_of(pe - 1);
   if (w0 == w1) return;  // finished inside one workgroup
+  const size_t off = ((size_t)T * kWave + lane) * 4;
   float m = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   constexpr int U = 4;  // pieces gathered per step, loads independent
@@ -424,7 +385,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(GlobalArgs a) {
       const float* ws = a.ws + (size_t)sl * kGSlotFloats;
       mi[u] = ws[kGH * kGD + h];
       li[u] = ws[kGH * kGD + kGH + h];
-      ai[u] = *reinterpret_cast<const f32x4*>(ws + (size_t)h * kGD + d0);
+      ai[u] = *reinterpret_cast<const f32x4*>(ws + off);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -437,23 +398,21 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(GlobalArgs a) {
       m = mn;
     }
   }
-  s_num[grp][tid % TPS] = num;
-  if (tid % TPS == 0) {
-    s_m[grp] = m;
-    s_den[grp] = den;
-  }
+  s_num[grp][lane] = num;
+  s_m[grp][lane] = m;
+  s_den[grp][lane] = den;
   __syncthreads();
   if (grp == 0) {
-    float M = s_m[0];
+    float M = s_m[0][lane];
 #pragma unroll
-    for (int gq = 1; gq < NG; ++gq) M = fmaxf(M, s_m[gq]);
+    for (int gq = 1; gq < NG; ++gq) M = fmaxf(M, s_m[gq][lane]);
     f32x4 n = {0.f, 0.f, 0.f, 0.f};
     float dd = 0.f;
 #pragma unroll
     for (int gq = 0; gq < NG; ++gq) {
-      const float f = (s_m[gq] == -INFINITY) ? 0.f : exp2_fast(s_m[gq] - M);
-      n += f * s_num[gq][tid];
-      dd += f * s_den[gq];
+      const float f = (s_m[gq][lane] == -INFINITY) ? 0.f : exp2_fast(s_m[gq][lane] - M);
+      n += f * s_num[gq][lane];
+      dd += f * s_den[gq][lane];
     }
     *reinterpret_cast<f32x4*>(ob) = n * (1.f / dd);
   }
@@ -461,7 +420,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(GlobalArgs a) {
 
 int global_num_splits(const da_shape& s, int num_cus) {
   if (s.num_splits > 0) return s.num_splits;
-  return 2 * num_cus;
+  return num_cus;  // one workgroup per compute unit
 }
 
 size_t global_workspace_bytes(const da_shape& s, int num_splits) {
@@ -489,15 +448,11 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   if (num_splits <= 1) return DA_OK;  // nothing was split: no merge
   // Expected pieces per sequence ~ G/B + 2: more pieces, more slot groups.
   const int est = num_splits / s.batch + 2;
-  const unsigned nb = (unsigned)s.batch * kGH;
-  if (est <= 16)
-    hipLaunchKernelGGL(lse_merge_kernel<128>, dim3(nb * 1), dim3(256), 0, stream, a);
-  else if (est <= 32)
-    hipLaunchKernelGGL(lse_merge_kernel<64>, dim3(nb * 2), dim3(256), 0, stream, a);
-  else if (est <= 64)
-    hipLaunchKernelGGL(lse_merge_kernel<32>, dim3(nb * 4), dim3(256), 0, stream, a);
+  const unsigned nb = (unsigned)s.batch * (kGPair * kGMTiles);
+  if (est <= 24)
+    hipLaunchKernelGGL(lse_merge_kernel<4>, dim3(nb), dim3(4 * kWave), 0, stream, a);
   else
-    hipLaunchKernelGGL(lse_merge_kernel<16>, dim3(nb * 8), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(lse_merge_kernel<16>, dim3(nb), dim3(16 * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 

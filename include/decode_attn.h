@@ -115,15 +115,20 @@ da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_
 
 /*
  * Bytes of device workspace attn_decode_global needs for `shape` on the
- * current device (per-split partial results: for each of 2*num_splits slots,
- * Hq*(D+2) fp32 values). Writes the size to *bytes.
+ * current device: a 16 KiB header (the batch's page prefix table) and, for
+ * each of 2*num_splits partial-result slots, Hq*(D+2) fp32 values. 0 when
+ * the call would use a single workgroup (nothing to merge). num_splits = 0
+ * asks for the default, one workgroup per compute unit of the current
+ * device. Writes the size to *bytes.
  */
 da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* bytes);
 
 /*
  * decodeGQA over a paged K=V cache (Gemma-4-12B global layers: Hkv = 1,
  * G = 16, D = 512, values equal keys).
- *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32.
+ *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32;
+ *   batch <= 256 (larger batches return DA_ERR_UNSUPPORTED; split them into
+ *   calls of at most 256 sequences); num_splits <= 65536.
  *   workspace: device memory of at least attn_decode_global_workspace_bytes
  *   (may be NULL when that size is 0). Its contents need no initialisation
  *   and are meaningless after the call.
