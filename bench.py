@@ -26,6 +26,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
+
+# HBM bytes one attn_decode_global call moves on this workload (main kernel +
+# merge kernel), from two rocprofv3 --pmc passes over this script: FETCH_SIZE
+# scaled by 2.0 and WRITE_SIZE by 1.0, the factors that make the same counters
+# read 512 MiB each for a 512 MiB device-to-device copy. Valid only for the
+# kernel sources they were taken on (hash below); reported as null otherwise.
+GLOBAL_TRAFFIC = {
+    "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
+    "sha256": "adde457eeda554bc4a9f6af98737332c10393c7f1f051036306eed27b209a0e4",
+    "bytes_per_call": 1173697331,
+}
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 
 
@@ -53,6 +64,17 @@ def global_bytes(wl):
     B, Hq = len(L), wl.Hkv * wl.G
     return dict(kv=int(L.sum()) * wl.Hkv * wl.D * esize, q=B * Hq * wl.D * esize,
                 out=B * Hq * wl.D * 4, table=int(((L + 15) // 16).sum()) * 4 + B * 4)
+
+
+def measured_traffic():
+    """HBM bytes per global call from the recorded counters, or None if the
+    kernel sources changed since they were taken."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GLOBAL_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return GLOBAL_TRAFFIC["bytes_per_call"] if h.hexdigest() == GLOBAL_TRAFFIC["sha256"] else None
 
 
 def to_dev(a):
@@ -191,6 +213,7 @@ def main():
         log(f"copied {args.copy_calibration_mib} MiB device-to-device for counter calibration")
         del src, dst
 
+    traffic = measured_traffic() if args.num_splits == 0 else None  # counters taken at the default split
     cpu = None
     if args.cpu_budget > 0:
         log(f"timing the oracle on a bounded sample (~{args.cpu_budget:.0f} s)")
@@ -223,6 +246,9 @@ def main():
             "global_frac_of_peak": round(g_ach / HBM_PEAK_GBS, 4),
             "bytes_per_step": step_bytes,
             "num_splits": args.num_splits,
+            "global_algorithmic_bytes_per_call": sum(gb.values()),
+            "global_traffic_over_algorithmic": (round(traffic / sum(gb.values()), 4)
+                                                if traffic is not None else None),
         },
         "roofline": {
             "kernel": "attn_decode_global (global_decode_kernel + lse_merge_kernel)",
@@ -231,7 +257,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(g_ach / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
     }
