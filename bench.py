@@ -36,6 +36,9 @@ GLOBAL_TRAFFIC = {
     "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
     "sha256": "adde457eeda554bc4a9f6af98737332c10393c7f1f051036306eed27b209a0e4",
     "bytes_per_call": 1173697331,
+    # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) of
+    # global_decode_kernel, from a third --pmc pass over the same sources
+    "mfma_busy": 0.105,
 }
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 
@@ -66,15 +69,14 @@ def global_bytes(wl):
                 out=B * Hq * wl.D * 4, table=int(((L + 15) // 16).sum()) * 4 + B * 4)
 
 
-def measured_traffic():
-    """HBM bytes per global call from the recorded counters, or None if the
-    kernel sources changed since they were taken."""
+def counters_current():
+    """True if the kernel sources are those the recorded counters were taken on."""
     import hashlib
     h = hashlib.sha256()
     for f in GLOBAL_TRAFFIC["sources"]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    return GLOBAL_TRAFFIC["bytes_per_call"] if h.hexdigest() == GLOBAL_TRAFFIC["sha256"] else None
+    return h.hexdigest() == GLOBAL_TRAFFIC["sha256"]
 
 
 def to_dev(a):
@@ -213,7 +215,8 @@ def main():
         log(f"copied {args.copy_calibration_mib} MiB device-to-device for counter calibration")
         del src, dst
 
-    traffic = measured_traffic() if args.num_splits == 0 else None  # counters taken at the default split
+    current = counters_current() and args.num_splits == 0  # counters taken at the default split
+    traffic = GLOBAL_TRAFFIC["bytes_per_call"] if current else None
     cpu = None
     if args.cpu_budget > 0:
         log(f"timing the oracle on a bounded sample (~{args.cpu_budget:.0f} s)")
@@ -249,6 +252,7 @@ def main():
             "global_algorithmic_bytes_per_call": sum(gb.values()),
             "global_traffic_over_algorithmic": (round(traffic / sum(gb.values()), 4)
                                                 if traffic is not None else None),
+            "global_mfma_busy": GLOBAL_TRAFFIC["mfma_busy"] if current else None,
         },
         "roofline": {
             "kernel": "attn_decode_global (global_decode_kernel + lse_merge_kernel)",
