@@ -173,8 +173,9 @@ def attn_decode_global_workspace_bytes(shape):
 def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=None, num_splits=0,
                        stream=None):
     """decodeGQA with values = keys. q [B, Hkv*G, D]; kv_cache tiled
-    [P, Hkv, D/x, 16, x]; returns out fp32 [B, Hkv*G, D]. The workspace is
-    allocated (and cached per device and size) when not given."""
+    [P, Hkv, D/x, 16, x]; returns out fp32 [B, Hkv*G, D]. When no workspace is
+    given, one is allocated and cached per device, stream and size (calls on
+    one stream run in order, so they may share it)."""
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (kv_cache,))
@@ -185,8 +186,9 @@ def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=N
     _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D),
              "out must be contiguous fp32 [B, Hq, D]")
     need = attn_decode_global_workspace_bytes(shape)
+    st = _stream(stream)
     if workspace is None and need > 0:
-        key = (q.device, need)
+        key = (q.device, st.value, need)
         workspace = _workspaces.get(key)
         if workspace is None:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -194,5 +196,5 @@ def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=N
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
-                                  ctypes.byref(shape), ws_ptr, ws_bytes, _stream(stream)))
+                                  ctypes.byref(shape), ws_ptr, ws_bytes, st))
     return out

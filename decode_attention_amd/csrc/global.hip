@@ -5,21 +5,26 @@
 // layers (scale 1, 16 query heads on 1 KV head, D = 512, values = keys).
 //
 // Work split. The cached pages of the whole batch form one list (sequence by
-// sequence); workgroup w of G takes pages [w*N/G, (w+1)*N/G). A sequence
-// that lies inside one workgroup's range is finished there; a sequence cut
-// by range boundaries leaves one partial result (unnormalised output, running
-// max m and sum l per head) per piece, and lse_merge_kernel combines them:
+// sequence); workgroup w of G takes the range of pages [w*N/G, (w+1)*N/G)
+// and walks it in steps of up to 4 pages of one sequence. A sequence that lies inside one range is finished there; a
+// sequence cut by range boundaries leaves one partial result (unnormalised
+// output, running max m and sum l per head) per piece, and lse_merge_kernel
+// combines them:
 //   M = max_i m_i,  o = sum_i 2^(m_i - M) acc_i / sum_i 2^(m_i - M) l_i
 // (scores are kept in the log2 domain). This is exact over the reals because
 // the softmax over a union of disjoint key sets factorises that way.
 //
+// The split is static: equal page counts per workgroup, one workgroup per
+// compute unit by default, and the result is reproducible bit for bit.
+//
 // A workgroup (one per compute unit) has 8 waves in 4 pairs. The pairs take
-// the pages of a segment round-robin, 4 pages per step, and all 8 waves meet
-// at one barrier per step, so no wave on the compute unit runs ahead of the
-// others; the 4 pair states are merged through LDS when the segment ends.
-// Inside a pair the 2 waves share a page: wave half h owns coordinates
-// [256h, 256h+256), i.e. 8 KB of the 16 KB page, loaded with lane-linear
-// 16-byte loads that land directly in the MFMA A-operand layout of K.
+// the pages of a step (pair p: page P + p), and all 8 waves meet at one
+// barrier per step, so no wave on the compute unit runs ahead of the others;
+// the 4 pair states are merged through LDS when a segment (the part of one
+// sequence inside a range) ends. Inside a pair the 2 waves share a page:
+// wave half h owns coordinates [256h, 256h+256), i.e. 8 KB of the 16 KB page,
+// loaded with lane-linear 16-byte loads that land directly in the MFMA
+// A-operand layout of K.
 //   S^T (16 tokens x 16 heads) = K Q^T : 8 x mfma_f32_16x16x32_bf16 per wave
 //     on its 256 coordinates; the 2 partial tiles are added through LDS in a
 //     fixed order, so both waves hold the same scores.
@@ -32,6 +37,9 @@
 //     16-row tile: its 32-wide k dimension holds the page's 16 tokens twice,
 //     against bf16(p) and against bf16(p - bf16(p)), so p enters the product
 //     to about 2^-17 relative.
+// Loads run ahead of the compute across segment and sequence boundaries:
+// page ids 4 steps, page slices 2 steps; a segment change costs a q reload
+// and an LDS merge, not a pipeline restart.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,7 +48,7 @@ namespace da {
 constexpr int kGD = 512;          // head dim
 constexpr int kGH = 16;           // query heads (KV head count 1)
 constexpr int kGPair = 2;         // waves sharing a page (coordinate halves)
-constexpr int kGPairs = 4;        // pairs per workgroup (4 pages per step)
+constexpr int kGPairs = 4;        // pairs per workgroup (up to 4 pages per step)
 constexpr int kGWaves = kGPair * kGPairs;
 constexpr int kGThreads = kGWaves * kWave;
 constexpr int kGSlice = kGD / kGPair;         // coordinates per wave (256)
@@ -53,15 +61,17 @@ constexpr int kGPageElems = kPage * kGD;      // bf16 elements per page (8192)
 constexpr int kGSlotFloats = kGH * kGD + 2 * kGH;
 constexpr int kGMaxBatch = 256;   // the model's batch domain is [1, 256]
 constexpr float kGRescale = 32.f;  // lazy-rescale threshold, log2 units
-constexpr int kGIdChunk = 4 * kWave;  // page ids gathered per refill (4 per lane); even
+constexpr int kGBuf = 3;          // page slices per wave in flight (ring, 2 ahead)
+constexpr int kGDesc = 6;         // step descriptors kept (ids are loaded 4 ahead)
+#ifndef DA_GLOBAL_VT_BATCH
+#define DA_GLOBAL_VT_BATCH 8
+#endif
+
+
 // Workspace: a header with the page prefix table (written by workgroup 0 of
 // the decode kernel, read by the merge), then 2*G partial-result slots.
 constexpr size_t kGHeaderBytes = 16384;  // >= (2*kGMaxBatch + 1) ints
 static_assert((2 * kGMaxBatch + 1) * sizeof(int) <= kGHeaderBytes, "header too small");
-#ifndef DA_GLOBAL_RING
-#define DA_GLOBAL_RING 3
-#endif
-constexpr int kGBuf = DA_GLOBAL_RING;  // pages held per wave (ring; kGBuf-1 ahead)
 
 struct GlobalArgs {
   const uint16_t* q;         // [B][16][512] bf16 bits
@@ -70,7 +80,7 @@ struct GlobalArgs {
   const int32_t* seq_lens;   // [B]
   float* out;                // [B][16][512]
   int* ws_hdr;               // [B+1] page prefix, then [B] clamped lengths
-  float* ws;                 // [2*G][kGSlotFloats]
+  float* ws;                 // [2*G][kGSlotFloats] partial slots
   int B, P_max, G;
 };
 
@@ -118,6 +128,17 @@ __device__ __forceinline__ int seq_of_page(const int* s_pre, int B, int p) {
   return lo;
 }
 
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+
+// x, opaque to the optimiser: addresses derived from it inside a rarely taken
+// branch are computed there, not hoisted out of the loop into registers that
+// would stay live across every step.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) void global_decode_kernel(GlobalArgs a) {
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
@@ -126,28 +147,27 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   // V slices, one per wave; also the merge area at the end of a segment
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][kGSlice * kPage];
   __shared__ float s_ml[4][2][kWave];           // m, l of the wave states being merged
+  // Q^T B operands of the current segment: [half][k-step][lane], lane h + 16g
+  // holding head h, coordinates 256*half + 32*kstep + 8g .. +8
+  __shared__ uint4 s_q[kGPair][kGKSteps][kWave];
 
   build_prefix(a, s_pre, s_len, s_tmp);
-  const int N = s_pre[a.B];
+  const int N = rfl(s_pre[a.B]);
   const int w = blockIdx.x;
   if (w == 0 && a.ws_hdr != nullptr) {  // publish the table for the merge kernel
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[i] = s_pre[i];
     for (int i = threadIdx.x; i < a.B; i += blockDim.x) a.ws_hdr[a.B + 1 + i] = s_len[i];
   }
-  const int r0 = range_start(w, N, a.G);
-  const int r1 = range_start(w + 1, N, a.G);
-  if (r0 >= r1) return;
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wv = rfl(threadIdx.x / kWave);
   const int pr = wv >> 1;          // pair
   const int hf = wv & 1;           // coordinate half of this wave
   const int hq = lane & 15;        // head of this lane's S^T / O^T column
   const int g = lane >> 4;         // token quad of this lane (S^T rows 4g..4g+3)
 
-  int ids[4] = {0, 0, 0, 0};       // physical ids of this pair's pages, 256 at a time
   uint4 buf[kGBuf][kGKSteps];      // ring of this wave's page slices
-  uint4 qreg[kGKSteps];            // Q^T B operands: head hq, d = 256hf + 32i + 8g .. +8
+  int idv[kGBuf];                  // physical page ids, 2 steps before their pages
   f32x4 acc[kGMTiles];             // O^T: head hq, d = 256hf + 16t + 4g + e
   float m_run = -INFINITY, l_run = 0.f;
   const size_t lane_off = (size_t)hf * kGKSteps * 512 + (size_t)lane * 8;
@@ -156,191 +176,274 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const int tr_tok = 4 * g + (s16 >> 2);
   const int tr_off = ((s16 & 3) >> 1) * 256 + tr_tok * 16 + (s16 & 1) * 8;  // + 512 t
 
-  auto issue = [&](int slot, int kk) {  // kk: step index inside the current id chunk
-    const int r = kk & (kWave - 1), q = kk >> 6;
-    const int i0 = __builtin_amdgcn_readlane(ids[0], r), i1 = __builtin_amdgcn_readlane(ids[1], r);
-    const int i2 = __builtin_amdgcn_readlane(ids[2], r), i3 = __builtin_amdgcn_readlane(ids[3], r);
-    const int phys = q == 0 ? i0 : q == 1 ? i1 : q == 2 ? i2 : i3;
-    const size_t base = (size_t)phys * kGPageElems + lane_off;
-#pragma unroll
-    for (int i = 0; i < kGKSteps; ++i) buf[slot][i] = ld16(a.kv + base + (size_t)i * 512);
-  };
+  // Step descriptors (uniform): first page, pages (0: no step), sequence,
+  // and whether the step opens a segment.
+  int dP[kGDesc], dN[kGDesc], dB[kGDesc], dS[kGDesc];
 
-  // s_part is double-buffered by step: consecutive steps alternate buffers
-  // (one barrier separates a buffer's reads from its next writes).
-  int xb = 0;
-  // One step for this pair: page j of the current sequence (L cached tokens)
-  // from ring slot `slot`; `valid` false when the pair has no page this step.
-  auto compute = [&](int slot, int j, bool valid, int L) {
-    f32x4 s2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  // This workgroup's range [R0, R1); segment state.
+  const int R0 = range_start(w, N, a.G), R1 = range_start(w + 1, N, a.G);
+  int xb = 0;                      // s_part buffer of the next step
+  bool seg_active = false;         // the pair states hold pages of segment seg_b
+  int seg_b = 0, seg_first = 0, seg_end = 0;
+
+  auto reset_state = [&]() __attribute__((always_inline)) {
+    m_run = -INFINITY;
+    l_run = 0.f;
 #pragma unroll
-    for (int i = 0; i < kGKSteps; ++i)
-      s2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[slot][i]),
-                                                          __builtin_bit_cast(bf16x8, qreg[i]), s2[i & 1],
-                                                          0, 0, 0);
-    s_part[xb][wv][lane] = s2[0] + s2[1];
+    for (int t = 0; t < kGMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Stage the query rows of sequence b in s_q (after the last use of the
+  // previous ones). Rare: waits for every outstanding load.
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const int tid = opaque(threadIdx.x);
+    uint4 t[2];
 #pragma unroll
-    for (int i = 0; i < kGKSteps; ++i) *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[slot][i];
-    const bool edge = !valid || (j + 1) * kPage > L;  // rare
-    if (edge && (!valid || j * kPage + (lane & 15) >= L)) {
-      // zero the V row of this lane's token (weight 0; 0 * NaN would poison)
-#pragma unroll
-      for (int i = 0; i < kGKSteps; ++i)
-        *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+    for (int r = 0; r < 2; ++r) {
+      const int u = 2 * tid + r;  // s_q element: half, k-step, lane
+      const int f = u / (kGKSteps * kWave), i = (u / kWave) % kGKSteps, l = u % kWave;
+      t[r] = ld16(a.q + ((size_t)b * kGH + (l & 15)) * kGD + f * kGSlice + 32 * i + 8 * (l >> 4));
     }
+    wait_vmem_all();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) (&s_q[0][0][0])[2 * tid + r] = t[r];
     __syncthreads();
-    const f32x4 s = s_part[xb][wv & ~1][lane] + s_part[xb][wv | 1][lane];
-    xb ^= 1;
-    if (!valid) return;  // uniform per pair; no barrier follows in this step
-    float sc[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sc[e] = s[e] * kLog2e;
-    if (edge) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (j * kPage + 4 * g + e >= L) sc[e] = -INFINITY;
-    }
-    // Lazy rescaling: m_run is a reference, not the exact running max. It
-    // moves (and the state is rescaled) only when a score exceeds it by more
-    // than kGRescale (log2 units), so p = 2^(s - m_run) stays below
-    // 2^kGRescale and no fp32 quantity can overflow; any reference gives the
-    // same softmax since numerator and denominator share it. The common case
-    // needs no cross-lane max. Always taken on a pair's first page.
-    const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    if (__any(lmax > m_run + kGRescale)) {
-      float mp = fmaxf(lmax, xor16(lmax));
-      mp = fmaxf(mp, xor32(mp));                                   // head max
-      const float m_new = (mp > m_run + kGRescale) ? mp : m_run;  // mp finite
-      const float alpha = exp2_fast(m_run - m_new);                // 0 from -inf
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int t = 0; t < kGMTiles; ++t) acc[t] *= alpha;
-    }
-    // P^T operand: k-slots 8g..8g+3 hold bf16(p) of tokens 4g..4g+3 and
-    // 8g+4..8g+7 the remainder bf16(p - bf16(p)); the V^T operand repeats the
-    // same 4 tokens in both halves.
-    bf16x8 pp;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pv = exp2_fast(sc[e] - m_run);
-      pp[e] = (__bf16)pv;
-      pp[4 + e] = (__bf16)(pv - (float)pp[e]);
-      l_run += pv;
-    }
-#pragma unroll
-    for (int t = 0; t < kGMTiles; ++t) {
-      const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)vs +
-                                                     t * 512 + tr_off));
-      const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v4, v4, 0, 1, 2, 3, 0, 1, 2, 3));
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pp, acc[t], 0, 0, 0);
-    }
   };
 
   // End-of-segment merge through LDS (the V regions are free by then): a
   // wave state is m (per head), l (lane partial) and its 16 accumulator tiles.
   f32x4* st = reinterpret_cast<f32x4*>(&s_v[0][0]);  // 4 states of [16][64] f32x4
-  auto put_state = [&](int k) {
+  auto put_state = [&](int k, int ln) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < kGMTiles; ++t) st[(k * kGMTiles + t) * kWave + lane] = acc[t];
-    s_ml[k][0][lane] = m_run;
-    s_ml[k][1][lane] = l_run;
+    for (int t = 0; t < kGMTiles; ++t) st[(k * kGMTiles + t) * kWave + ln] = acc[t];
+    s_ml[k][0][ln] = m_run;
+    s_ml[k][1][ln] = l_run;
   };
-  auto take_state = [&](int k) {  // fold stored state k into this one
-    const float m_o = s_ml[k][0][lane], l_o = s_ml[k][1][lane];
+  auto take_state = [&](int k, int ln) __attribute__((always_inline)) {  // fold stored state k into this one
+    const float m_o = s_ml[k][0][ln], l_o = s_ml[k][1][ln];
     const float M = fmaxf(m_run, m_o);
     const float fs = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - M);
     const float fo = (m_o == -INFINITY) ? 0.f : exp2_fast(m_o - M);
 #pragma unroll
-    for (int t = 0; t < kGMTiles; ++t) acc[t] = acc[t] * fs + st[(k * kGMTiles + t) * kWave + lane] * fo;
+    for (int t = 0; t < kGMTiles; ++t) acc[t] = acc[t] * fs + st[(k * kGMTiles + t) * kWave + ln] * fo;
     l_run = l_run * fs + l_o * fo;
     m_run = M;
   };
-
-  int b = seq_of_page(s_pre, a.B, r0);
-  for (int s0 = r0; s0 < r1;) {
-    while (s_pre[b + 1] <= s0) ++b;  // uniform; skips empty sequences
-    const int pb = __builtin_amdgcn_readfirstlane(s_pre[b]);
-    const int pe = __builtin_amdgcn_readfirstlane(s_pre[b + 1]);
-    const int L = __builtin_amdgcn_readfirstlane(s_len[b]);
-    const int s1 = min(r1, pe);                            // segment [s0, s1) of sequence b
-    const int nsteps = (s1 - s0 + kGPairs - 1) / kGPairs;  // this pair's page of step k: s0 + 4k + pr
-    {
-      const uint16_t* qb = a.q + ((size_t)b * kGH + hq) * kGD + hf * kGSlice + 8 * g;
-#pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) qreg[i] = ld16(qb + 32 * i);
-    }
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int t = 0; t < kGMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < nsteps; c0 += kGIdChunk) {
-      const int cn = min(nsteps - c0, kGIdChunk);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = c0 + q * kWave + lane;
-        const int pg = s0 + kGPairs * k + pr;  // a step past the end loads the first page again
-        ids[q] = a.bt[(size_t)b * a.P_max + (k < nsteps && pg < s1 ? pg : s0) - pb];
-      }
-      wait_vmem_all();
-      // Ring of kGBuf steps, kGBuf-1 ahead; loads past the chunk's end are
-      // clamped to its last step (redundant, cache-resident) so that every
-      // pass issues the same loads and the compiler waits only for the slot
-      // in use.
-#pragma unroll
-      for (int u = 0; u < kGBuf - 1; ++u) issue(u, min(u, cn - 1));
-      for (int base = 0; base < cn; base += kGBuf) {
-#pragma unroll
-        for (int u = 0; u < kGBuf; ++u) {
-          const int kk = base + u;
-          issue((u + kGBuf - 1) % kGBuf, min(kk + kGBuf - 1, cn - 1));
-          if (kk < cn) {
-            const int pg = s0 + kGPairs * (c0 + kk) + pr;
-            compute(u, pg - pb, pg < s1, L);
-          }
-        }
-      }
-    }
-    // Merge the 4 pair states (same coordinate half): 2 -> 0 and 3 -> 1, then 1 -> 0.
+  // Merge the 4 pair states (2 -> 0 and 3 -> 1, then 1 -> 0) and write the
+  // segment [seg_first, seg_end) of sequence seg_b: the output row if it is
+  // the whole sequence, else a partial slot of this workgroup (the first
+  // segment of the range in slot 2w, the last in slot 2w + 1).
+  auto flush = [&]() __attribute__((always_inline)) {
+    const int ln = opaque(lane), lh = ln & 15, lg = ln >> 4;
     __syncthreads();  // every wave is done with its V region
-    if (pr >= 2) put_state((pr - 2) * kGPair + hf);
+    if (pr >= 2) put_state((pr - 2) * kGPair + hf, ln);
     __syncthreads();
-    if (pr < 2) take_state(pr * kGPair + hf);
+    if (pr < 2) take_state(pr * kGPair + hf, ln);
     __syncthreads();
-    if (pr == 1) put_state(hf);
+    if (pr == 1) put_state(hf, ln);
     __syncthreads();
     if (pr == 0) {
-      take_state(hf);
+      take_state(hf, ln);
       float lt = l_run + xor16(l_run);
       lt += xor32(lt);
-      if (s0 == pb && s1 == pe) {  // whole sequence in this workgroup: o[b][h][d]
-        float* dst = a.out + ((size_t)b * kGH + hq) * kGD + hf * kGSlice + 4 * g;
+      const int pb = rfl(s_pre[seg_b]), pe = rfl(s_pre[seg_b + 1]);
+      if (seg_first == pb && seg_end == pe) {  // whole sequence: o[b][h][d]
+        float* dst = a.out + ((size_t)seg_b * kGH + lh) * kGD + hf * kGSlice + 4 * lg;
         const float inv = 1.f / lt;
 #pragma unroll
         for (int t = 0; t < kGMTiles; ++t) *reinterpret_cast<f32x4*>(dst + t * 16) = acc[t] * inv;
-      } else {                     // partial slot, lane order: 1 KB contiguous per store
-        float* ws = a.ws + (size_t)(2 * w + (s0 == r0 ? 0 : 1)) * kGSlotFloats;
-        if (hf == 0 && g == 0) {
-          ws[kGH * kGD + hq] = m_run;
-          ws[kGH * kGD + kGH + hq] = lt;
+      } else {  // partial slot, lane order: 1 KB contiguous per store
+        const int slot = 2 * w + (seg_first == R0 ? 0 : 1);
+        float* ws = a.ws + (size_t)slot * kGSlotFloats;
+        if (hf == 0 && lg == 0) {
+          ws[kGH * kGD + lh] = m_run;
+          ws[kGH * kGD + kGH + lh] = lt;
         }
 #pragma unroll
         for (int t = 0; t < kGMTiles; ++t)
-          *reinterpret_cast<f32x4*>(ws + ((size_t)(hf * kGMTiles + t) * kWave + lane) * 4) = acc[t];
+          *reinterpret_cast<f32x4*>(ws + ((size_t)(hf * kGMTiles + t) * kWave + ln) * 4) = acc[t];
       }
     }
+    wait_vmem_all();
     __syncthreads();  // the merge area is page space again
-    s0 = s1;
+    reset_state();
+    seg_active = false;
+  };
+
+  if (R0 < R1) {
+    const int t_end = R1;
+    int gp = R0, gb = seq_of_page(s_pre, a.B, R0);
+    size_t last_idx = 0;
+
+    // Next step descriptor into slot d: up to 4 pages of one sequence from
+    // page gp on, or no step (0 pages) past the range's end.
+    auto gen = [&](int d) __attribute__((always_inline)) {
+      int n = 0, nw = 0;
+      if (gp < t_end) {
+        while (rfl(s_pre[gb + 1]) <= gp) ++gb;
+        const int pe = rfl(s_pre[gb + 1]);
+        n = min(kGPairs, min(pe, t_end) - gp);
+        nw = (gp == rfl(s_pre[gb]) || gp == R0) ? 1 : 0;
+      }
+      dP[d] = gp;
+      dN[d] = n;
+      dB[d] = gb;
+      dS[d] = nw;
+      gp += n;
+    };
+    // This pair's page id of step d (a past-the-end step repeats the last id).
+    auto load_id = [&](int is, int d) __attribute__((always_inline)) {
+      if (dN[d] > 0) {
+        const int b = dB[d];
+        last_idx = (size_t)b * a.P_max + (size_t)(dP[d] + min(pr, dN[d] - 1) - rfl(s_pre[b]));
+      }
+      size_t idx = last_idx;
+      // a vector load: a scalar one would be waited for by every LDS wait
+      asm volatile("" : "+v"(idx));
+      idv[is] = a.bt[idx];
+    };
+    auto issue = [&](int bs, int is) __attribute__((always_inline)) {
+      const int phys = rfl(idv[is]);
+      const size_t base = (size_t)phys * kGPageElems + lane_off;
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i) buf[bs][i] = ld16(a.kv + base + (size_t)i * 512);
+    };
+    // One step from ring slot bs and descriptor d. Returns false for a step
+    // past the range's end; the open segment is then flushed outside the
+    // ring loop, where the ring's registers are free.
+    auto compute = [&](int bs, int d) __attribute__((always_inline)) -> bool {
+      const int P = dP[d], n = dN[d], b = dB[d];
+      const int pb = rfl(s_pre[b]);
+      const int L = rfl(s_len[b]);
+      const int j = P + pr - pb;  // this pair's page within sequence b
+      // all LDS reads first, then the MFMAs (the scheduler would otherwise
+      // pay the LDS latency once per MFMA)
+      uint4 qv[kGKSteps];
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i) qv[i] = s_q[hf][i][lane];
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 s2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i)
+        s2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[bs][i]),
+                                                            __builtin_bit_cast(bf16x8, qv[i]), s2[i & 1],
+                                                            0, 0, 0);
+      s_part[xb][wv][lane] = s2[0] + s2[1];
+#pragma unroll
+      for (int i = 0; i < kGKSteps; ++i) *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[bs][i];
+      const bool edge = pr < n && (j + 1) * kPage > L;  // rare: the sequence's last page
+      if (edge && j * kPage + (lane & 15) >= L) {
+        // zero the V row of this lane's token (weight 0; 0 * NaN would poison)
+#pragma unroll
+        for (int i = 0; i < kGKSteps; ++i)
+          *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = make_uint4(0u, 0u, 0u, 0u);
+      }
+      __syncthreads();
+      const f32x4 s = s_part[xb][wv & ~1][lane] + s_part[xb][wv | 1][lane];
+      xb ^= 1;
+      if (n == 0) return false;  // past the end: the open segment is flushed after the loop
+      if (!seg_active) {
+        seg_active = true;
+        seg_b = b;
+        seg_first = P;
+      }
+      seg_end = P + n;
+      if (pr < n) {
+        float sc[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = s[e] * kLog2e;
+        if (edge) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j * kPage + 4 * g + e >= L) sc[e] = -INFINITY;
+        }
+        // Lazy rescaling: m_run is a reference, not the exact running max.
+        // It moves (and the state is rescaled) only when a score exceeds it
+        // by more than kGRescale (log2 units), so p = 2^(s - m_run) stays
+        // below 2^kGRescale and no fp32 quantity can overflow; any reference
+        // gives the same softmax since numerator and denominator share it.
+        // The common case needs no cross-lane max. Always taken on a pair's
+        // first page of a segment.
+        const float lmax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        if (__any(lmax > m_run + kGRescale)) {
+          float mp = fmaxf(lmax, xor16(lmax));
+          mp = fmaxf(mp, xor32(mp));                                   // head max
+          const float m_new = (mp > m_run + kGRescale) ? mp : m_run;  // mp finite
+          const float alpha = exp2_fast(m_run - m_new);                // 0 from -inf
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < kGMTiles; ++t) acc[t] *= alpha;
+        }
+        // P^T operand: k-slots 8g..8g+3 hold bf16(p) of tokens 4g..4g+3 and
+        // 8g+4..8g+7 the remainder bf16(p - bf16(p)); the V^T operand
+        // repeats the same 4 tokens in both halves.
+        bf16x8 pp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float pv = exp2_fast(sc[e] - m_run);
+          pp[e] = (__bf16)pv;
+          pp[4 + e] = (__bf16)(pv - (float)pp[e]);
+          l_run += pv;
+        }
+        constexpr int kVB = DA_GLOBAL_VT_BATCH;  // transposed reads in flight per batch
+#pragma unroll
+        for (int t0 = 0; t0 < kGMTiles; t0 += kVB) {
+          s16x4 v4[kVB];
+#pragma unroll
+          for (int u = 0; u < kVB; ++u)
+            v4[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)vs +
+                                                           (t0 + u) * 512 + tr_off));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < kVB; ++u) {
+            const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v4[u], v4[u], 0, 1, 2, 3, 0, 1, 2, 3));
+            acc[t0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pp, acc[t0 + u], 0, 0, 0);
+          }
+        }
+      }
+      const int dn = (d + 1) % kGDesc;
+      if (dS[dn]) {  // the next step opens another segment: finish this one
+        flush();
+        load_q(dB[dn]);
+      }
+      return true;
+    };
+
+    // Prologue: descriptors 0..3, ids 0..3, pages of steps 0, 1.
+#pragma unroll
+    for (int d = 0; d < 4; ++d) gen(d);
+    reset_state();
+    load_q(dB[0]);
+    load_id(0, 0);
+    load_id(1, 1);
+    load_id(2, 2);
+    issue(0, 0);
+    issue(1, 1);
+    load_id(0, 3);
+    // Step k = k0 + u: ring slot k % 3, descriptor k % 6. Every pass issues
+    // the same loads; steps past the range's end reload its last page.
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kGDesc; ++u) {
+        gen((u + 4) % kGDesc);
+        load_id((u + 4) % kGBuf, (u + 4) % kGDesc);
+        issue((u + 2) % kGBuf, (u + 2) % kGBuf);
+        if (!compute(u % kGBuf, u)) goto range_done;
+      }
+    }
+  range_done:
+    wait_vmem_all();
+    if (seg_active) flush();
   }
 }
 
 // Log-sum-exp merge of the partial results of split sequences. Workgroup:
 // (sequence b, output tile T = 16 coordinates of all 16 heads, i.e. one
 // lane-order tile of a partial slot); its NG groups of 64 threads fold the
-// sequence's pieces w0+grp, w0+grp+NG, ... with a running max, reading 1 KB
-// contiguous per piece, and are then combined the same way. The page prefix
-// table comes from the workspace header.
+// sequence's pieces grp, grp+NG, ... with a running max, reading 1 KB
+// contiguous per piece, and are then combined the same way. The pieces are
+// found from the page prefix table in the workspace header.
 template <int NG>
 __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   constexpr int kTiles = kGPair * kGMTiles;   // 32 tiles of 16 coordinates
@@ -361,27 +464,34 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   }
   const int N = pre[a.B];
   const int pb = pre[b], pe = pre[b + 1];
-  // workgroup whose range holds page p: largest w with range_start(w) <= p
-  auto wg_of = [&](int p) { return (int)((((long long)p + 1) * a.G - 1) / N); };
-  const int w0 = wg_of(pb), w1 = wg_of(pe - 1);
-  if (w0 == w1) return;  // finished inside one workgroup
+  // workgroup whose range holds page p: the largest w with range_start(w) <= p
+  auto wg_of = [&](int p) __attribute__((always_inline)) { return (int)((((long long)p + 1) * a.G - 1) / N); };
+  const int w0 = wg_of(pb);
+  const int np = wg_of(pe - 1) - w0 + 1;  // pieces
+  if (np == 1) return;  // finished inside one workgroup: the row is written
+  // slot of piece i, or -1 for an empty range
+  auto slot_of = [&](int i) __attribute__((always_inline)) -> int {
+    const int ww = w0 + i;
+    const int rs = range_start(ww, N, a.G);
+    if (rs == range_start(ww + 1, N, a.G)) return -1;  // empty range: no piece
+    return 2 * ww + ((i == 0 && rs != pb) ? 1 : 0);
+  };
   const size_t off = ((size_t)T * kWave + lane) * 4;
   float m = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   constexpr int U = 4;  // pieces gathered per step, loads independent
-  for (int w = w0 + grp; w <= w1; w += U * NG) {
+  for (int i = grp; i < np; i += U * NG) {
     float mi[U], li[U];
     f32x4 ai[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ww = w + u * NG;
+      const int ii = i + u * NG;
       mi[u] = -INFINITY;
       li[u] = 0.f;
       ai[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (ww > w1) continue;
-      const int rs = range_start(ww, N, a.G);
-      if (rs == range_start(ww + 1, N, a.G)) continue;  // empty range: no piece
-      const int sl = 2 * ww + ((ww == w0 && rs != pb) ? 1 : 0);
+      if (ii >= np) continue;
+      const int sl = slot_of(ii);
+      if (sl < 0) continue;
       const float* ws = a.ws + (size_t)sl * kGSlotFloats;
       mi[u] = ws[kGH * kGD + h];
       li[u] = ws[kGH * kGD + kGH + h];

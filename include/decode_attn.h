@@ -129,6 +129,10 @@ da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* byte
  *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32;
  *   batch <= 256 (larger batches return DA_ERR_UNSUPPORTED; split them into
  *   calls of at most 256 sequences); num_splits <= 65536.
+ *   Work split: the cached pages of the batch are divided into equal,
+ *   contiguous ranges, one per workgroup (num_splits of them, or one per
+ *   compute unit when num_splits = 0); the output is reproducible bit for
+ *   bit for a given split.
  *   workspace: device memory of at least attn_decode_global_workspace_bytes
  *   (may be NULL when that size is 0). Its contents need no initialisation
  *   and are meaningless after the call.

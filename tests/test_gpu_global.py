@@ -82,7 +82,8 @@ def test_diffuse_softmax(gpu_lib, mode):
 
 def test_deterministic(gpu_lib):
     wl = I.make_global([10000, 3, 777], kv_dtype="bf16", tag=(404,), **I.GLOBAL)
-    assert np.array_equal(global_on_gpu(wl), global_on_gpu(wl))
+    for splits in (0, 37, 256):
+        assert np.array_equal(global_on_gpu(wl, splits), global_on_gpu(wl, splits))
 
 
 def test_config2_full_size_sampled(gpu_lib):
