@@ -177,8 +177,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const int tr_off = ((s16 & 3) >> 1) * 256 + tr_tok * 16 + (s16 & 1) * 8;  // + 512 t
 
   // Step descriptors (uniform): first page, pages (0: no step), sequence,
-  // and whether the step opens a segment.
-  int dP[kGDesc], dN[kGDesc], dB[kGDesc], dS[kGDesc];
+  // whether the step opens a segment, page index of the first page within its
+  // sequence, and the sequence's length.
+  int dP[kGDesc], dN[kGDesc], dB[kGDesc], dS[kGDesc], dJ[kGDesc], dL[kGDesc];
 
   // This workgroup's range [R0, R1); segment state.
   const int R0 = range_start(w, N, a.G), R1 = range_start(w + 1, N, a.G);
@@ -272,6 +273,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   if (R0 < R1) {
     const int t_end = R1;
     int gp = R0, gb = seq_of_page(s_pre, a.B, R0);
+    // first page, end page and length of sequence gb (read again only when
+    // the generator moves to another sequence)
+    int gpb = rfl(s_pre[gb]), gpe = rfl(s_pre[gb + 1]), gL = rfl(s_len[gb]);
     size_t last_idx = 0;
 
     // Next step descriptor into slot d: up to 4 pages of one sequence from
@@ -279,23 +283,26 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     auto gen = [&](int d) __attribute__((always_inline)) {
       int n = 0, nw = 0;
       if (gp < t_end) {
-        while (rfl(s_pre[gb + 1]) <= gp) ++gb;
-        const int pe = rfl(s_pre[gb + 1]);
-        n = min(kGPairs, min(pe, t_end) - gp);
-        nw = (gp == rfl(s_pre[gb]) || gp == R0) ? 1 : 0;
+        while (gpe <= gp) {  // next sequence with pages
+          ++gb;
+          gpb = gpe;
+          gpe = rfl(s_pre[gb + 1]);
+          gL = rfl(s_len[gb]);
+        }
+        n = min(kGPairs, min(gpe, t_end) - gp);
+        nw = (gp == gpb || gp == R0) ? 1 : 0;
       }
       dP[d] = gp;
       dN[d] = n;
       dB[d] = gb;
       dS[d] = nw;
+      dJ[d] = gp - gpb;
+      dL[d] = gL;
       gp += n;
     };
     // This pair's page id of step d (a past-the-end step repeats the last id).
     auto load_id = [&](int is, int d) __attribute__((always_inline)) {
-      if (dN[d] > 0) {
-        const int b = dB[d];
-        last_idx = (size_t)b * a.P_max + (size_t)(dP[d] + min(pr, dN[d] - 1) - rfl(s_pre[b]));
-      }
+      if (dN[d] > 0) last_idx = (size_t)dB[d] * a.P_max + (size_t)(dJ[d] + min(pr, dN[d] - 1));
       size_t idx = last_idx;
       // a vector load: a scalar one would be waited for by every LDS wait
       asm volatile("" : "+v"(idx));
@@ -312,9 +319,8 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     // ring loop, where the ring's registers are free.
     auto compute = [&](int bs, int d) __attribute__((always_inline)) -> bool {
       const int P = dP[d], n = dN[d], b = dB[d];
-      const int pb = rfl(s_pre[b]);
-      const int L = rfl(s_len[b]);
-      const int j = P + pr - pb;  // this pair's page within sequence b
+      const int L = dL[d];
+      const int j = dJ[d] + pr;  // this pair's page within sequence b
       // all LDS reads first, then the MFMAs (the scheduler would otherwise
       // pay the LDS latency once per MFMA)
       uint4 qv[kGKSteps];
