@@ -34,11 +34,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 # kernel sources they were taken on (hash below); reported as null otherwise.
 GLOBAL_TRAFFIC = {
     "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
-    "sha256": "adde457eeda554bc4a9f6af98737332c10393c7f1f051036306eed27b209a0e4",
-    "bytes_per_call": 1173697331,
+    "sha256": "130d0ee2092f4cfddc84832f32bfeff89355bc35c28799b0d3a1e7c4d0971c64",
+    "bytes_per_call": 1171856998,
     # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) of
     # global_decode_kernel, from a third --pmc pass over the same sources
-    "mfma_busy": 0.105,
+    "mfma_busy": 0.108,
 }
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 
