@@ -14,13 +14,19 @@ Sources (the pages are data; every formula here is restated, not pasted):
   ``slidingDecodeGQA`` (decode over the last ``w`` cached positions; no Lean
   definition of its own, semantics from ``slidingGQA``).
 * Model Spec page of gemma-4-12b, "Compute-graph nodes" (``attn.core`` rows:
-  scale 1, head map h/2 and h/16) and "Tensors of the main nodes" (q, k, v,
-  seq_lens, o shapes).
+  scale 1, head map h/2 and h/16; ``attn.qk_norm``, ``attn.v_norm`` and
+  ``attn.rope`` rows: eps, theta, rot, denom, active) and "Tensors of the
+  main nodes" (q, k, v, seq_lens, o shapes).
+* Op Specs page, ``Norm.lean`` (``rms``, ``rmsnorm``, ``rmsnormUnit``),
+  ``Rope.lean`` (``invFreq``, ``rope``) and ``Attention.lean``
+  (``sigmoidGate``); Op Specs overview, "Scalar functions" (``sigmoid``).
 
-Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
-something other than itself (literal brute force over the Lean predicates,
-50-digit mpmath evaluation, torch's scaled_dot_product_attention as a library
-special case, closed forms and invariants). No function is "parity unpinned".
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_norm_rope.py`` against something other than itself
+(literal brute force over the Lean predicates, 50-digit mpmath evaluation,
+torch's scaled_dot_product_attention and rms_norm and a rotate-half RoPE from
+transformers as library special cases, complex-number rotation, closed forms
+and invariants). No function is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -37,4 +43,21 @@ from .paged import (  # noqa: F401
     sliding_visible_range,
     paged_decode_sliding,
     paged_decode_global,
+)
+from .norm_rope import (  # noqa: F401
+    rms,
+    rmsnorm,
+    rmsnorm_unit,
+    inv_freq,
+    rope,
+    sigmoid,
+    sigmoid_gate,
+)
+from .append import (  # noqa: F401
+    EPS,
+    SLIDING_ROPE,
+    GLOBAL_ROPE,
+    decode_step_qkv_sliding,
+    decode_step_qk_global,
+    append_targets,
 )
