@@ -44,7 +44,7 @@ class DaShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
-           "attn_status_string")
+           "attn_kv_append_sliding", "attn_kv_append_global", "attn_status_string")
 
 
 def library_path():
@@ -72,6 +72,10 @@ def load_library():
         lib.attn_decode_global_workspace_bytes.argtypes = [ctypes.POINTER(DaShape),
                                                            ctypes.POINTER(ctypes.c_size_t)]
         lib.attn_decode_global_workspace_bytes.restype = ctypes.c_int32
+        lib.attn_kv_append_sliding.argtypes = [vp] * 10 + [ctypes.POINTER(DaShape), vp]
+        lib.attn_kv_append_sliding.restype = ctypes.c_int32
+        lib.attn_kv_append_global.argtypes = [vp] * 8 + [ctypes.POINTER(DaShape), vp]
+        lib.attn_kv_append_global.restype = ctypes.c_int32
         lib.attn_status_string.argtypes = [ctypes.c_int32]
         lib.attn_status_string.restype = ctypes.c_char_p
         del i32p
@@ -198,3 +202,78 @@ def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=N
     _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
                                   ctypes.byref(shape), ws_ptr, ws_bytes, st))
     return out
+
+
+def _check_f32(name, t, shape, device):
+    import torch
+    _require(t.dtype == torch.float32 and t.is_contiguous() and t.device == device and tuple(t.shape) == shape,
+             f"{name} must be contiguous fp32 {list(shape)} on the caches' device")
+
+
+def attn_kv_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, block_table, positions, k_cache, v_cache,
+                           q_out=None, stream=None):
+    """Norm + RoPE of the new tokens of a sliding layer and their append:
+    q_raw fp32 [B, Hq, 256], k_raw/v_raw fp32 [B, Hkv, 256], w_q/w_k fp32
+    [256], positions int32 [B]; writes k/v into their slots of k_cache/v_cache
+    [P, Hkv, 16, 256] and returns q_out [B, Hq, 256] in the caches' dtype."""
+    import torch
+    lib = load_library()
+    _require(k_cache.dim() == 4 and k_cache.shape == v_cache.shape and k_cache.shape[2] == PAGE_SIZE
+             and k_cache.is_contiguous() and v_cache.is_contiguous() and k_cache.dtype == v_cache.dtype
+             and k_cache.is_cuda and v_cache.device == k_cache.device,
+             "k_cache/v_cache must be contiguous [P, Hkv, 16, D] on one device")
+    P, Hkv, _, D = k_cache.shape
+    B, Hq = q_raw.shape[0], q_raw.shape[1]
+    dev = k_cache.device
+    _check_f32("q_raw", q_raw, (B, Hq, D), dev)
+    _check_f32("k_raw", k_raw, (B, Hkv, D), dev)
+    _check_f32("v_raw", v_raw, (B, Hkv, D), dev)
+    _check_f32("w_q", w_q, (D,), dev)
+    _check_f32("w_k", w_k, (D,), dev)
+    _require(Hq % Hkv == 0, "head shape mismatch")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+             and block_table.shape[0] == B and block_table.device == dev, "block_table must be int32 [B, P_max]")
+    _require(positions.dtype == torch.int32 and tuple(positions.shape) == (B,) and positions.is_contiguous()
+             and positions.device == dev, "positions must be int32 [B]")
+    if q_out is None:
+        q_out = torch.empty((B, Hq, D), dtype=k_cache.dtype, device=dev)
+    _require(q_out.dtype == k_cache.dtype and q_out.is_contiguous() and tuple(q_out.shape) == (B, Hq, D),
+             "q_out must be contiguous [B, Hq, D] in the caches' dtype")
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(k_cache))
+    _check(lib.attn_kv_append_sliding(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(w_q), _ptr(w_k),
+                                      _ptr(block_table), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(q_out), ctypes.byref(shape), _stream(stream)))
+    return q_out
+
+
+def attn_kv_append_global(q_raw, kv_raw, w_q, w_k, block_table, positions, kv_cache, q_out=None, stream=None):
+    """Norm + RoPE of the new tokens of a global layer and the append of k to
+    the tiled K=V cache [P, Hkv, D/x, 16, x]: q_raw fp32 [B, Hq, 512], kv_raw
+    fp32 [B, Hkv, 512], w_q/w_k fp32 [512], positions int32 [B]; returns q_out
+    [B, Hq, 512] in the cache's dtype."""
+    import torch
+    lib = load_library()
+    _require(kv_cache.dim() == 5 and kv_cache.shape[3] == PAGE_SIZE and kv_cache.is_contiguous()
+             and kv_cache.is_cuda, "kv_cache must be contiguous tiled [P, Hkv, D/x, 16, x]")
+    P, Hkv, nx, _, x = kv_cache.shape
+    D = nx * x
+    B, Hq = q_raw.shape[0], q_raw.shape[1]
+    dev = kv_cache.device
+    _check_f32("q_raw", q_raw, (B, Hq, D), dev)
+    _check_f32("kv_raw", kv_raw, (B, Hkv, D), dev)
+    _check_f32("w_q", w_q, (D,), dev)
+    _check_f32("w_k", w_k, (D,), dev)
+    _require(Hq % Hkv == 0 and x * kv_cache.element_size() == 16, "head shape mismatch")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+             and block_table.shape[0] == B and block_table.device == dev, "block_table must be int32 [B, P_max]")
+    _require(positions.dtype == torch.int32 and tuple(positions.shape) == (B,) and positions.is_contiguous()
+             and positions.device == dev, "positions must be int32 [B]")
+    if q_out is None:
+        q_out = torch.empty((B, Hq, D), dtype=kv_cache.dtype, device=dev)
+    _require(q_out.dtype == kv_cache.dtype and q_out.is_contiguous() and tuple(q_out.shape) == (B, Hq, D),
+             "q_out must be contiguous [B, Hq, D] in the cache's dtype")
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(kv_cache))
+    _check(lib.attn_kv_append_global(_ptr(q_raw), _ptr(kv_raw), _ptr(w_q), _ptr(w_k), _ptr(block_table),
+                                     _ptr(positions), _ptr(kv_cache), _ptr(q_out), ctypes.byref(shape),
+                                     _stream(stream)))
+    return q_out

@@ -117,6 +117,39 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                            (hipStream_t)stream);
 }
 
+da_status attn_kv_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw, const float* w_q,
+                                 const float* w_k, const int32_t* block_table, const int32_t* positions,
+                                 void* k_cache, void* v_cache, void* q_out, const da_shape* shape, void* stream) {
+  da_status st = check_common(shape);
+  if (st != DA_OK) return st;
+  if (!q_raw || !k_raw || !v_raw || !w_q || !w_k || !block_table || !positions || !k_cache || !v_cache ||
+      !q_out)
+    return DA_ERR_INVALID_ARG;
+  if (shape->head_dim != 256) return DA_ERR_UNSUPPORTED;
+  if ((long long)shape->batch * shape->num_kv_heads * (shape->group + 2) > 0x7FFFFFFFLL) return DA_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  return da::launch_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, block_table, positions, k_cache, v_cache, q_out,
+                                   *shape, (hipStream_t)stream);
+}
+
+da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const float* w_q, const float* w_k,
+                                const int32_t* block_table, const int32_t* positions, void* kv_cache, void* q_out,
+                                const da_shape* shape, void* stream) {
+  da_status st = check_common(shape);
+  if (st != DA_OK) return st;
+  if (!q_raw || !kv_raw || !w_q || !w_k || !block_table || !positions || !kv_cache || !q_out)
+    return DA_ERR_INVALID_ARG;
+  if (shape->head_dim != 512) return DA_ERR_UNSUPPORTED;
+  if ((long long)shape->batch * shape->num_kv_heads * (shape->group + 1) > 0x7FFFFFFFLL) return DA_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  return da::launch_append_global(q_raw, kv_raw, w_q, w_k, block_table, positions, kv_cache, q_out, *shape,
+                                  (hipStream_t)stream);
+}
+
 const char* attn_status_string(da_status status) {
   switch (status) {
     case DA_OK: return "ok";

@@ -22,4 +22,12 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
                         const int32_t* seq_lens, void* out, const da_shape& s, int num_splits,
                         void* workspace, hipStream_t stream);
 
+// Decode-step norm + RoPE of the new tokens and their append to the caches.
+da_status launch_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw, const float* w_q,
+                                const float* w_k, const int32_t* block_table, const int32_t* positions,
+                                void* k_cache, void* v_cache, void* q_out, const da_shape& s, hipStream_t stream);
+da_status launch_append_global(const float* q_raw, const float* kv_raw, const float* w_q, const float* w_k,
+                               const int32_t* block_table, const int32_t* positions, void* kv_cache, void* q_out,
+                               const da_shape& s, hipStream_t stream);
+
 }  // namespace da

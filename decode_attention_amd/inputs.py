@@ -292,6 +292,81 @@ def make_global(seq_lens, *, Hkv=1, G=16, D=512, kv_dtype="bf16", tag=(200,),
 
 
 # ----------------------------------------------------------------------------
+# decode-step inputs of the new token (before its norms and rotary embedding)
+# ----------------------------------------------------------------------------
+
+STREAM_RAW_Q, STREAM_RAW_K, STREAM_RAW_V, STREAM_FILL = 7, 8, 9, 10
+
+
+@dataclass
+class AppendWorkload:
+    kind: str                # "sliding" (separate k/v caches) or "global" (one K=V cache)
+    q_raw: np.ndarray        # float32 [B, Hkv*G, D]
+    k_raw: np.ndarray        # float32 [B, Hkv, D] (the kv projection on global layers)
+    v_raw: object            # float32 [B, Hkv, D], or None on global layers
+    w_q: np.ndarray          # float32 [D]
+    w_k: np.ndarray          # float32 [D]
+    positions: np.ndarray    # int32 [B]
+    block_table: np.ndarray  # int32 [B, P_max]
+    k_cache: np.ndarray      # stored; sliding [P, Hkv, 16, D], global tiled [P, Hkv, D/x, 16, x]
+    v_cache: object          # stored [P, Hkv, 16, D], or None on global layers
+    kv_dtype: str
+    Hkv: int
+    G: int
+    D: int
+
+
+def raw_rows(rng, shape):
+    """Pre-norm projection rows: N(0, s^2) with a per-row scale s drawn
+    log-uniformly in [0.1, 10] (the norm must undo it)."""
+    s = np.exp(rng.uniform(np.log(0.1), np.log(10.0), size=shape[:-1] + (1,)))
+    return (rng.standard_normal(shape) * s).astype(np.float32)
+
+
+def make_append(kind, positions, *, Hkv, G, D, kv_dtype="bf16", tag=(500,), layer=0,
+                P_max=None, block_table=None, k_cache=None, v_cache=None):
+    """New-token inputs for ``kind`` ("sliding" or "global") at ``positions``.
+
+    Without caches: every sequence with a valid position gets a page of its
+    own for that position, the other block-table entries point at page 0, and
+    the caches hold random stored values (so that writes to any other place
+    show). With ``block_table`` and caches given (e.g. from make_sliding or
+    make_global), those are copied and used as they are."""
+    positions = np.asarray(positions, dtype=np.int32)
+    B = len(positions)
+    sep = kind == "sliding"
+    dt = storage_np_dtype(kv_dtype)
+    if block_table is None:
+        if P_max is None:
+            P_max = max(1, int(np.max(positions, initial=0)) // PAGE + 1)
+        num_pages = B + 4
+        perm = rng_for(tag, layer, STREAM_PERM).permutation(num_pages)
+        bt = np.zeros((B, P_max), dtype=np.int32)
+        for b, p in enumerate(positions):
+            if 0 <= p < P_max * PAGE:
+                bt[b, p // PAGE] = perm[b]
+        rf = rng_for(tag, layer, STREAM_FILL)
+        if sep:
+            k_cache = to_storage(rf.standard_normal((num_pages, Hkv, PAGE, D)).astype(np.float32), kv_dtype)
+            v_cache = to_storage(rf.standard_normal((num_pages, Hkv, PAGE, D)).astype(np.float32), kv_dtype)
+        else:
+            x = chunk_elems(kv_dtype)
+            k_cache = to_storage(rf.standard_normal((num_pages, Hkv, D // x, PAGE, x)).astype(np.float32), kv_dtype)
+            v_cache = None
+    else:
+        bt = np.array(block_table, dtype=np.int32, copy=True)
+        k_cache = np.array(k_cache, dtype=dt, copy=True)
+        v_cache = np.array(v_cache, dtype=dt, copy=True) if sep else None
+    q_raw = raw_rows(rng_for(tag, layer, STREAM_RAW_Q), (B, Hkv * G, D))
+    k_raw = raw_rows(rng_for(tag, layer, STREAM_RAW_K), (B, Hkv, D))
+    v_raw = raw_rows(rng_for(tag, layer, STREAM_RAW_V), (B, Hkv, D)) if sep else None
+    w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D).astype(np.float32)
+    w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D).astype(np.float32)
+    return AppendWorkload(kind, q_raw, k_raw, v_raw, w_q, w_k, positions, bt, k_cache, v_cache,
+                          kv_dtype, Hkv, G, D)
+
+
+# ----------------------------------------------------------------------------
 # named configurations (Gemma-4-12B shapes)
 # ----------------------------------------------------------------------------
 

@@ -143,6 +143,50 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                              const int32_t* seq_lens, void* out, const da_shape* shape,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode-step preparation of the new token of every sequence on a sliding
+ * layer (pages: Op Specs of google/gemma-4-12B, Norm.lean rmsnorm and
+ * rmsnormUnit, Rope.lean rope; gemma-4-12b Model Spec, attn.qk_norm,
+ * attn.v_norm and attn.rope rows of the sliding layers):
+ *   q = rope(rmsnorm(q_raw) * w_q),  k = rope(rmsnorm(k_raw) * w_k),
+ *   v = rmsnormUnit(v_raw),
+ * per head, eps 1e-6, rope with theta 10^4 on all 256 coordinates (pairs
+ * (i, i + 128), all 128 frequencies) at position positions[b]. q is written
+ * to q_out; k and v are stored in slot positions[b] % 16 of page
+ * block_table[b][positions[b] / 16] of k_cache and v_cache (row-major pages,
+ * as attn_decode_sliding reads them). The token at position p is the
+ * (p+1)-th cached token: call attn_decode_sliding afterwards with
+ * seq_lens[b] = positions[b] + 1.
+ *   q_raw [batch][Hkv*G][256], k_raw and v_raw [batch][Hkv][256], w_q and
+ *   w_k [256]: fp32. q_out [batch][Hkv*G][256] and the caches: kv_dtype
+ *   (bf16 values are rounded to nearest even). positions: int32 [batch].
+ *   Sequences with positions[b] outside [0, 16*max_pages_per_seq) are left
+ *   untouched (no q_out row, no cache write).
+ *   Built shapes: head_dim 256, any Hkv and G. The block-table entry read must
+ *   be a page of the pool; no other cache element is written.
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_NO_DEVICE or
+ * DA_ERR_LAUNCH.
+ */
+da_status attn_kv_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw,
+                                 const float* w_q, const float* w_k, const int32_t* block_table,
+                                 const int32_t* positions, void* k_cache, void* v_cache, void* q_out,
+                                 const da_shape* shape, void* stream);
+
+/*
+ * The same for a global layer (gemma-4-12b Model Spec, attn.qk_norm and
+ * attn.rope rows of the global layers): one 512-wide projection kv_raw per
+ * sequence and KV head is both k and v; q = rope(rmsnorm(q_raw) * w_q) and
+ * k = rope(rmsnorm(kv_raw) * w_k) with theta 10^6 and only the first 64 of
+ * the 256 frequencies active (pairs (i, i + 256), i < 64, rotated; the rest
+ * unchanged). k is stored in the tiled K=V cache that attn_decode_global
+ * reads as both keys and values.
+ *   q_raw [batch][Hkv*G][512], kv_raw [batch][Hkv][512], w_q and w_k [512]:
+ *   fp32. Built shapes: head_dim 512. Other conventions as above.
+ */
+da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const float* w_q,
+                                const float* w_k, const int32_t* block_table, const int32_t* positions,
+                                void* kv_cache, void* q_out, const da_shape* shape, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(da_status status);
 

@@ -43,6 +43,7 @@ from .paged import (  # noqa: F401
     sliding_visible_range,
     paged_decode_sliding,
     paged_decode_global,
+    f64_to_bf16_bits,
 )
 from .norm_rope import (  # noqa: F401
     rms,

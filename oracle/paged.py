@@ -125,3 +125,17 @@ def paged_decode_global(q, kv_cache, block_table, seq_lens, kv_dtype, scale=1.0)
         o = decode_gqa(scale, qf[b].reshape(Hkv, G, D), k, k)
         out[b] = o.reshape(Hq, D)
     return out
+
+
+def f64_to_bf16_bits(x):
+    """bf16 bit patterns of float64 values rounded to nearest, ties to even,
+    in one step (no intermediate float32). Domain: finite values within the
+    normal bf16 range, as the appended rows are."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    bits = x.view(np.uint64)
+    drop = np.uint64(52 - 7)  # fp64 keeps 52 mantissa bits, bf16 keeps 7
+    half = np.uint64(1) << (drop - np.uint64(1))
+    r = ((bits >> drop) & np.uint64(1)) + half - np.uint64(1)
+    rounded = ((bits + r) >> drop) << drop  # the carry moves into the exponent as it should
+    y = rounded.view(np.float64).astype(np.float32)  # exact: y has 8 significant bits
+    return (y.view(np.uint32) >> np.uint32(16)).astype(np.uint16)

@@ -111,3 +111,32 @@ def test_no_device_reported_after_valid_arguments(lib):
     assert glob(lib, _gshape()) == -4
     n = ctypes.c_size_t(0)
     assert lib.attn_decode_global_workspace_bytes(ctypes.byref(_gshape()), ctypes.byref(n)) == -4
+
+
+def append_sliding(lib, shape, ptrs=None):
+    p = ptrs or [FAKE] * 10
+    return lib.attn_kv_append_sliding(*p, ctypes.byref(shape) if shape is not None else None, NULL)
+
+
+def append_global(lib, shape, ptrs=None):
+    p = ptrs or [FAKE] * 8
+    return lib.attn_kv_append_global(*p, ctypes.byref(shape) if shape is not None else None, NULL)
+
+
+def test_append_validation(lib):
+    assert append_sliding(lib, None) == -1
+    assert append_sliding(lib, _shape(batch=0)) == -1
+    assert append_sliding(lib, _shape(), ptrs=[FAKE] * 9 + [NULL]) == -1
+    assert append_sliding(lib, _shape(head_dim=512)) == -2
+    assert append_global(lib, None) == -1
+    assert append_global(lib, _gshape(), ptrs=[NULL] + [FAKE] * 7) == -1
+    assert append_global(lib, _gshape(head_dim=256)) == -2
+    s = _gshape()
+    s.page_size = 8
+    assert append_global(lib, s) == -2
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_append_no_device_reported_after_valid_arguments(lib):
+    assert append_sliding(lib, _shape()) == -4
+    assert append_global(lib, _gshape()) == -4

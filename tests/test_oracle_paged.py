@@ -149,3 +149,17 @@ def test_block_table_pages_are_distinct_and_guard_is_poisoned():
     assert len(set(used.tolist())) == len(used) and guard not in used
     assert np.all(wl.block_table[0, 3:] == guard)
     assert np.isnan(P.stored_to_f64(wl.kv_cache[guard], "bf16")).all()
+
+
+def test_f64_to_bf16_rounding():
+    from decode_attention_amd import inputs as I
+    import torch
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.140625, 1.0 + 2**-8 + 2**-40])
+    got = oracle.f64_to_bf16_bits(x)
+    # exact values stay, midpoints tie to even, and just above a midpoint rounds
+    # up (rounding through float32 first would lose the 2^-40 and tie down)
+    assert [int(v) for v in got] == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x4049, 0x3F81]
+    r = np.random.default_rng(3).standard_normal(100000).astype(np.float32)
+    ref_torch = torch.tensor(r).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(r.astype(np.float64)), ref_torch)
+    np.testing.assert_array_equal(oracle.f64_to_bf16_bits(r.astype(np.float64)), I.f32_to_bf16_bits(r))
