@@ -44,6 +44,7 @@ class DaShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
+           "attn_decode_sliding_gated", "attn_decode_global_gated",
            "attn_kv_append_sliding", "attn_kv_append_global", "attn_status_string")
 
 
@@ -69,6 +70,12 @@ def load_library():
         lib.attn_decode_global.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
                                            ctypes.c_size_t, vp]
         lib.attn_decode_global.restype = ctypes.c_int32
+        lib.attn_decode_sliding_gated.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp,
+                                                  ctypes.POINTER(DaShape), vp]
+        lib.attn_decode_sliding_gated.restype = ctypes.c_int32
+        lib.attn_decode_global_gated.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
+                                                 ctypes.c_size_t, vp]
+        lib.attn_decode_global_gated.restype = ctypes.c_int32
         lib.attn_decode_global_workspace_bytes.argtypes = [ctypes.POINTER(DaShape),
                                                            ctypes.POINTER(ctypes.c_size_t)]
         lib.attn_decode_global_workspace_bytes.restype = ctypes.c_int32
@@ -136,10 +143,29 @@ def _check_common(q, block_table, seq_lens, caches):
     _require(block_table.shape[0] == q.shape[0] and seq_lens.shape[0] == q.shape[0], "batch mismatch")
 
 
+def _check_gate(gate, out):
+    import torch
+    _require(gate.dtype == torch.float32 and gate.is_contiguous() and gate.device == out.device
+             and gate.shape == out.shape, "gate must be contiguous fp32 with out's shape, on out's device")
+    g0, o0 = gate.data_ptr(), out.data_ptr()
+    n = out.numel() * 4
+    _require(g0 + n <= o0 or o0 + n <= g0, "gate must not overlap out")
+
+
 def attn_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out=None, stream=None):
     """slidingDecodeGQA. q [B, Hkv*G, D]; k_cache, v_cache [P, Hkv, 16, D]
     (row-major pages); block_table int32 [B, P_max]; seq_lens int32 [B].
     Returns out fp32 [B, Hkv*G, D] (allocated if not given)."""
+    return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, None, out, stream)
+
+
+def attn_decode_sliding_gated(q, k_cache, v_cache, block_table, seq_lens, window, gate, out=None, stream=None):
+    """attn_decode_sliding followed by sigmoidGate: out = o * sigmoid(gate),
+    gate fp32 [B, Hkv*G, D]."""
+    return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stream)
+
+
+def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stream):
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (k_cache, v_cache))
@@ -153,9 +179,15 @@ def attn_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out=
     _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D),
              "out must be contiguous fp32 [B, Hq, D]")
     shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q))
-    _check(lib.attn_decode_sliding(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                   _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),
-                                   _stream(stream)))
+    if gate is None:
+        _check(lib.attn_decode_sliding(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),
+                                       _stream(stream)))
+    else:
+        _check_gate(gate, out)
+        _check(lib.attn_decode_sliding_gated(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                             _ptr(seq_lens), int(window), _ptr(gate), _ptr(out),
+                                             ctypes.byref(shape), _stream(stream)))
     return out
 
 
@@ -180,6 +212,17 @@ def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=N
     [P, Hkv, D/x, 16, x]; returns out fp32 [B, Hkv*G, D]. When no workspace is
     given, one is allocated and cached per device, stream and size (calls on
     one stream run in order, so they may share it)."""
+    return _global(q, kv_cache, block_table, seq_lens, None, out, workspace, num_splits, stream)
+
+
+def attn_decode_global_gated(q, kv_cache, block_table, seq_lens, gate, out=None, workspace=None, num_splits=0,
+                             stream=None):
+    """attn_decode_global followed by sigmoidGate: out = o * sigmoid(gate),
+    gate fp32 [B, Hkv*G, D]."""
+    return _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits, stream)
+
+
+def _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits, stream):
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (kv_cache,))
@@ -199,8 +242,13 @@ def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=N
             _workspaces[key] = workspace
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
-                                  ctypes.byref(shape), ws_ptr, ws_bytes, st))
+    if gate is None:
+        _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                      ctypes.byref(shape), ws_ptr, ws_bytes, st))
+    else:
+        _check_gate(gate, out)
+        _check(lib.attn_decode_global_gated(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+                                            _ptr(gate), _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st))
     return out
 
 

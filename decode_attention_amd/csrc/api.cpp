@@ -68,13 +68,9 @@ da_status check_global_shape(const da_shape* s) {
   return DA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* block_table, const int32_t* seq_lens, int32_t window,
-                              void* out, const da_shape* shape, void* stream) {
+da_status decode_sliding(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                         const int32_t* seq_lens, int32_t window, const float* gate, void* out,
+                         const da_shape* shape, void* stream) {
   da_status st = check_common(shape);
   if (st != DA_OK) return st;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
@@ -84,8 +80,41 @@ da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_
   int dev = 0, cus = 0;
   st = current_device(&dev, &cus);
   if (st != DA_OK) return st;
-  return da::launch_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out, *shape,
+  return da::launch_sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, *shape,
                             (hipStream_t)stream);
+}
+
+da_status decode_global(const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                        const float* gate, void* out, const da_shape* shape, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  da_status st = check_global_shape(shape);
+  if (st != DA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  const int splits = da::global_num_splits(*shape, cus);
+  const size_t need = da::global_workspace_bytes(*shape, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
+  return da::launch_global(q, kv_cache, block_table, seq_lens, gate, out, *shape, splits, workspace,
+                           (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* seq_lens, int32_t window,
+                              void* out, const da_shape* shape, void* stream) {
+  return decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, nullptr, out, shape, stream);
+}
+
+da_status attn_decode_sliding_gated(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens, int32_t window,
+                                    const float* gate, void* out, const da_shape* shape, void* stream) {
+  if (!gate) return DA_ERR_INVALID_ARG;
+  return decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, shape, stream);
 }
 
 da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* bytes) {
@@ -104,17 +133,15 @@ da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* byte
 da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t* block_table,
                              const int32_t* seq_lens, void* out, const da_shape* shape,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  da_status st = check_global_shape(shape);
-  if (st != DA_OK) return st;
-  if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
-  int dev = 0, cus = 0;
-  st = current_device(&dev, &cus);
-  if (st != DA_OK) return st;
-  const int splits = da::global_num_splits(*shape, cus);
-  const size_t need = da::global_workspace_bytes(*shape, splits);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
-  return da::launch_global(q, kv_cache, block_table, seq_lens, out, *shape, splits, workspace,
-                           (hipStream_t)stream);
+  return decode_global(q, kv_cache, block_table, seq_lens, nullptr, out, shape, workspace, workspace_bytes,
+                       stream);
+}
+
+da_status attn_decode_global_gated(const void* q, const void* kv_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, const float* gate, void* out, const da_shape* shape,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!gate) return DA_ERR_INVALID_ARG;
+  return decode_global(q, kv_cache, block_table, seq_lens, gate, out, shape, workspace, workspace_bytes, stream);
 }
 
 da_status attn_kv_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw, const float* w_q,

@@ -83,6 +83,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
                                          acc, false);
 }
 
+// sigmoid(x) = 1 / (1 + exp(-x)); exp(-x) = inf for very negative x gives 0.
+__device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x)); }
+
 // ---------------------------------------------------------------- memory
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 

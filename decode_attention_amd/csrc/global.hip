@@ -79,6 +79,7 @@ struct GlobalArgs {
   const int32_t* bt;         // [B][P_max]
   const int32_t* seq_lens;   // [B]
   float* out;                // [B][16][512]
+  const float* gate;         // [B][16][512] sigmoidGate epilogue, or null
   int* ws_hdr;               // [B+1] page prefix, then [B] clamped lengths
   float* ws;                 // [2*G][kGSlotFloats] partial slots
   int B, P_max, G;
@@ -251,7 +252,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
         float* dst = a.out + ((size_t)seg_b * kGH + lh) * kGD + hf * kGSlice + 4 * lg;
         const float inv = 1.f / lt;
 #pragma unroll
-        for (int t = 0; t < kGMTiles; ++t) *reinterpret_cast<f32x4*>(dst + t * 16) = acc[t] * inv;
+        for (int t = 0; t < kGMTiles; ++t) {
+          f32x4 o = acc[t] * inv;
+          if (a.gate) {  // sigmoidGate epilogue
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (dst - a.out) + t * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
+          }
+          *reinterpret_cast<f32x4*>(dst + t * 16) = o;
+        }
       } else {  // partial slot, lane order: 1 KB contiguous per store
         const int slot = 2 * w + (seg_first == R0 ? 0 : 1);
         float* ws = a.ws + (size_t)slot * kGSlotFloats;
@@ -530,7 +539,13 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
       n += f * s_num[gq][lane];
       dd += f * s_den[gq][lane];
     }
-    *reinterpret_cast<f32x4*>(ob) = n * (1.f / dd);
+    f32x4 o = n * (1.f / dd);
+    if (a.gate) {  // sigmoidGate epilogue
+      const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (ob - a.out));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
+    }
+    *reinterpret_cast<f32x4*>(ob) = o;
   }
 }
 
@@ -546,14 +561,15 @@ size_t global_workspace_bytes(const da_shape& s, int num_splits) {
 }
 
 da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
-                        const int32_t* seq_lens, void* out, const da_shape& s, int num_splits,
-                        void* workspace, hipStream_t stream) {
+                        const int32_t* seq_lens, const float* gate, void* out, const da_shape& s,
+                        int num_splits, void* workspace, hipStream_t stream) {
   GlobalArgs a;
   a.q = (const uint16_t*)q;
   a.kv = (const uint16_t*)kv_cache;
   a.bt = block_table;
   a.seq_lens = seq_lens;
   a.out = (float*)out;
+  a.gate = gate;
   a.ws_hdr = num_splits > 1 ? (int*)workspace : nullptr;
   a.ws = num_splits > 1 ? (float*)((char*)workspace + kGHeaderBytes) : nullptr;
   a.B = s.batch;

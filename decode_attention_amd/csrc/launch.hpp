@@ -10,17 +10,18 @@ namespace da {
 
 constexpr int kPageSizeAbi = 16;  // tokens per page the kernels are built for
 
+// gate: fp32 [B][Hq][D] for the sigmoidGate epilogue, or null.
 da_status launch_sliding(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, const int32_t* seq_lens, int32_t window, void* out,
-                         const da_shape& s, hipStream_t stream);
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t window, const float* gate,
+                         void* out, const da_shape& s, hipStream_t stream);
 
 // Number of workgroups the global kernel divides the batch's pages among.
 int global_num_splits(const da_shape& s, int num_cus);
 size_t global_workspace_bytes(const da_shape& s, int num_splits);
 
 da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
-                        const int32_t* seq_lens, void* out, const da_shape& s, int num_splits,
-                        void* workspace, hipStream_t stream);
+                        const int32_t* seq_lens, const float* gate, void* out, const da_shape& s,
+                        int num_splits, void* workspace, hipStream_t stream);
 
 // Decode-step norm + RoPE of the new tokens and their append to the caches.
 da_status launch_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw, const float* w_q,

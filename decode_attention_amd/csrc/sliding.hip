@@ -75,7 +75,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int window,
-    float* __restrict__ out, int Hkv, int P_max) {
+    const float* __restrict__ gate, float* __restrict__ out, int Hkv, int P_max) {
   constexpr int G = 2;
   constexpr int E = Elem<T>::E;
   constexpr int CPR = D / E;
@@ -97,6 +97,7 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
   // Lengths beyond the block-table row are clamped so no read leaves it.
   const int L = min(seq_lens[b], P_max * kPage);
   float* ob = out + ((size_t)b * Hkv * G + (size_t)c * G) * D;
+  const float* gb = gate ? gate + ((size_t)b * Hkv * G + (size_t)c * G) * D : nullptr;
   if (L <= 0 || window <= 0) {  // no visible key: the output rows are 0
     for (int i = threadIdx.x; i < G * D; i += NW * kWave) ob[i] = 0.f;
     return;
@@ -243,26 +244,27 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
       num = fmaf(f, s_acc[w][h][d], num);
       den = fmaf(f, s_l[w][h], den);
     }
-    ob[idx] = num / den;
+    const float o = num / den;
+    ob[idx] = gb ? o * sigmoidf(gb[idx]) : o;  // sigmoidGate epilogue
   }
 }
 
 constexpr int kSlidingWaves = 4;
 
 da_status launch_sliding(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_table, const int32_t* seq_lens, int32_t window, void* out,
-                         const da_shape& s, hipStream_t stream) {
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t window, const float* gate,
+                         void* out, const da_shape& s, hipStream_t stream) {
   const dim3 grid((unsigned)s.batch * (unsigned)s.num_kv_heads);
   const dim3 block(kSlidingWaves * kWave);
   if (s.kv_dtype == DA_DTYPE_BF16) {
     hipLaunchKernelGGL((sliding_decode_kernel<uint16_t, 256, kSlidingWaves>), grid, block, 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
-                       block_table, seq_lens, window, (float*)out, s.num_kv_heads,
+                       block_table, seq_lens, window, gate, (float*)out, s.num_kv_heads,
                        s.max_pages_per_seq);
   } else {
     hipLaunchKernelGGL((sliding_decode_kernel<float, 256, kSlidingWaves>), grid, block, 0, stream,
                        (const float*)q, (const float*)k_cache, (const float*)v_cache, block_table,
-                       seq_lens, window, (float*)out, s.num_kv_heads, s.max_pages_per_seq);
+                       seq_lens, window, gate, (float*)out, s.num_kv_heads, s.max_pages_per_seq);
   }
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }

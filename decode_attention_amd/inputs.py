@@ -323,6 +323,15 @@ def raw_rows(rng, shape):
     return (rng.standard_normal(shape) * s).astype(np.float32)
 
 
+STREAM_GATE = 11
+
+
+def make_gate(shape, tag=(600,), layer=0, scale=2.0):
+    """Output-gate logits [B, Hq, D]: float32 N(0, scale^2), so sigmoid(gate)
+    spans most of (0, 1)."""
+    return (rng_for(tag, layer, STREAM_GATE).standard_normal(shape) * scale).astype(np.float32)
+
+
 def make_append(kind, positions, *, Hkv, G, D, kv_dtype="bf16", tag=(500,), layer=0,
                 P_max=None, block_table=None, k_cache=None, v_cache=None):
     """New-token inputs for ``kind`` ("sliding" or "global") at ``positions``.

@@ -144,6 +144,24 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_sliding and attn_decode_global followed by the output gate of
+ * gated attention, o * sigmoid(gate) elementwise (pages: Op Specs of
+ * google/gemma-4-12B, Attention.lean sigmoidGate; Op Specs overview, "Scalar
+ * functions", sigmoid(x) = 1 / (1 + exp(-x))), applied where each output row
+ * is written. gate: fp32 device array [batch][Hkv*G][D], the layout of out;
+ * it must not overlap out. A NULL gate is an invalid argument. Everything
+ * else as for the ungated calls.
+ */
+da_status attn_decode_sliding_gated(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    int32_t window, const float* gate, void* out,
+                                    const da_shape* shape, void* stream);
+da_status attn_decode_global_gated(const void* q, const void* kv_cache, const int32_t* block_table,
+                                   const int32_t* seq_lens, const float* gate, void* out,
+                                   const da_shape* shape, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Decode-step preparation of the new token of every sequence on a sliding
  * layer (pages: Op Specs of google/gemma-4-12B, Norm.lean rmsnorm and
  * rmsnormUnit, Rope.lean rope; gemma-4-12b Model Spec, attn.qk_norm,

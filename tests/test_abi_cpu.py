@@ -140,3 +140,29 @@ def test_append_validation(lib):
 def test_append_no_device_reported_after_valid_arguments(lib):
     assert append_sliding(lib, _shape()) == -4
     assert append_global(lib, _gshape()) == -4
+
+
+def sliding_gated(lib, shape, gate=FAKE, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return lib.attn_decode_sliding_gated(p[0], p[1], p[2], p[3], p[4], 1024, gate, p[5],
+                                         ctypes.byref(shape), NULL)
+
+
+def global_gated(lib, shape, gate=FAKE, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return lib.attn_decode_global_gated(p[0], p[1], p[2], p[3], gate, p[4], ctypes.byref(shape),
+                                        FAKE, 1 << 30, NULL)
+
+
+def test_gated_validation(lib):
+    assert sliding_gated(lib, _shape(), gate=NULL) == -1
+    assert sliding_gated(lib, _shape(), ptrs=[FAKE] * 5 + [NULL]) == -1
+    assert sliding_gated(lib, _shape(head_dim=512)) == -2
+    assert global_gated(lib, _gshape(), gate=NULL) == -1
+    assert global_gated(lib, _gshape(group=8)) == -2
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_gated_no_device_reported_after_valid_arguments(lib):
+    assert sliding_gated(lib, _shape()) == -4
+    assert global_gated(lib, _gshape()) == -4
