@@ -34,11 +34,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 # kernel sources they were taken on (hash below); reported as null otherwise.
 GLOBAL_TRAFFIC = {
     "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
-    "sha256": "130d0ee2092f4cfddc84832f32bfeff89355bc35c28799b0d3a1e7c4d0971c64",
-    "bytes_per_call": 1171856998,
+    "sha256": "37dca9c4d5d54c0eb0f3f9efeeffd72f0f72d7b2a6f4532b181ae45590131c68",
+    "bytes_per_call": 1174063392,
     # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) of
     # global_decode_kernel, from a third --pmc pass over the same sources
-    "mfma_busy": 0.108,
+    "mfma_busy": 0.1065,
 }
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 
@@ -67,6 +67,31 @@ def global_bytes(wl):
     B, Hq = len(L), wl.Hkv * wl.G
     return dict(kv=int(L.sum()) * wl.Hkv * wl.D * esize, q=B * Hq * wl.D * esize,
                 out=B * Hq * wl.D * 4, table=int(((L + 15) // 16).sum()) * 4 + B * 4)
+
+
+def append_bytes(aw):
+    """Algorithmic bytes of one decode-step append: fp32 projections, norm
+    weights, positions and one block-table entry per sequence in; q and the
+    new k (and v) rows out in the cache dtype."""
+    esize = 2 if aw.kv_dtype == "bf16" else 4
+    B, Hq = len(aw.positions), aw.Hkv * aw.G
+    kv_rows = (2 if aw.v_raw is not None else 1) * B * aw.Hkv
+    return (B * Hq + kv_rows) * aw.D * (4 + esize) + 2 * aw.D * 4 + 2 * B * 4
+
+
+def time_calls(fn, n):
+    """Mean µs per call of fn over n back-to-back calls (HIP events on the
+    current stream, after one untimed call)."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
 
 
 def counters_current():
@@ -132,6 +157,45 @@ def cpu_baseline(sl, gl, sl_bytes_fn, gl_bytes_fn, budget_s):
     }
 
 
+def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_splits):
+    """The decode-step appends and the gated variants, timed after the step
+    (not part of it): one new token per sequence at position L, the gate on
+    the same outputs."""
+    import torch
+    log("timing the decode-step appends and the gated calls")
+    shp = dict(Hkv=sl.Hkv, G=sl.G, D=sl.D)
+    aws = I.make_append("sliding", sl.seq_lens, kv_dtype="bf16", tag=(700,), **shp)
+    awg = I.make_append("global", gl.seq_lens, kv_dtype="bf16", tag=(701,), **I.GLOBAL)
+    d_as = [to_dev(x) for x in (aws.q_raw, aws.k_raw, aws.v_raw, aws.w_q, aws.w_k, aws.block_table,
+                                aws.positions, aws.k_cache, aws.v_cache)]
+    d_ag = [to_dev(x) for x in (awg.q_raw, awg.k_raw, awg.w_q, awg.w_k, awg.block_table, awg.positions,
+                                awg.k_cache)]
+    q_as = torch.empty((64, 16, 256), dtype=torch.bfloat16, device="cuda")
+    q_ag = torch.empty((64, 16, 512), dtype=torch.bfloat16, device="cuda")
+    gate_sl = to_dev(I.make_gate(sl.q.shape, tag=(702,)))
+    gate_gl = to_dev(I.make_gate(gl.q.shape, tag=(703,)))
+    app_sl_us = time_calls(lambda: da.attn_kv_append_sliding(*d_as, q_out=q_as), n_extra)
+    app_gl_us = time_calls(lambda: da.attn_kv_append_global(*d_ag, q_out=q_ag), n_extra)
+    gsl_us = time_calls(lambda: da.attn_decode_sliding_gated(*d_sl[:5], sl.window, gate_sl, out=out_sl), n_extra)
+    ggl_us = time_calls(lambda: da.attn_decode_global_gated(*d_gl, gate_gl, out=out_gl,
+                                                            num_splits=num_splits), n_extra)
+    gate_b = 64 * 16 * 4
+    extra = {
+        "append_sliding_us_per_call": round(app_sl_us, 2),
+        "append_sliding_GBps": round(append_bytes(aws) / (app_sl_us * 1e-6) / 1e9, 1),
+        "append_global_us_per_call": round(app_gl_us, 2),
+        "append_global_GBps": round(append_bytes(awg) / (app_gl_us * 1e-6) / 1e9, 1),
+        "sliding_gated_us_per_call": round(gsl_us, 2),
+        "sliding_gated_GBps": round((sum(sb.values()) + gate_b * 256) / (gsl_us * 1e-6) / 1e9, 1),
+        "global_gated_us_per_call": round(ggl_us, 2),
+        "global_gated_GBps": round((sum(gb.values()) + gate_b * 512) / (ggl_us * 1e-6) / 1e9, 1),
+    }
+    log(f"append sliding {app_sl_us:.1f} us, append global {app_gl_us:.1f} us, "
+        f"gated sliding {gsl_us:.1f} us, gated global {ggl_us:.1f} us")
+
+    return extra
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +206,9 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once, so that a "
                          "counter profile holds a plain copy of known size to scale HBM counters")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the append and gated-call timings after the step (so that a kernel "
+                         "trace holds the step's dispatches only)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
@@ -215,6 +282,9 @@ def main():
         log(f"copied {args.copy_calibration_mib} MiB device-to-device for counter calibration")
         del src, dst
 
+    extra = {} if args.no_extras else time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb,
+                                                  max(args.steps, 10), args.num_splits)
+
     current = counters_current() and args.num_splits == 0  # counters taken at the default split
     traffic = GLOBAL_TRAFFIC["bytes_per_call"] if current else None
     cpu = None
@@ -253,6 +323,7 @@ def main():
             "global_traffic_over_algorithmic": (round(traffic / sum(gb.values()), 4)
                                                 if traffic is not None else None),
             "global_mfma_busy": GLOBAL_TRAFFIC["mfma_busy"] if current else None,
+            **extra,
         },
         "roofline": {
             "kernel": "attn_decode_global (global_decode_kernel + lse_merge_kernel)",

@@ -254,7 +254,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
         for (int t = 0; t < kGMTiles; ++t) {
           f32x4 o = acc[t] * inv;
-          if (a.gate) {  // sigmoidGate epilogue
+          if (a.gate) {  // sigmoidGate epilogue (set only when no merge follows)
             const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (dst - a.out) + t * 16);
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
@@ -471,6 +471,14 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   const int h = lane & 15, g = lane >> 4;
   const int d0 = (T / kGMTiles) * kGSlice + (T % kGMTiles) * 16 + 4 * g;
   float* ob = a.out + ((size_t)b * kGH + h) * kGD + d0;
+  // sigmoidGate epilogue operands, loaded first so that their latency hides
+  // behind the header reads: the gate, and the row as the decode kernel wrote
+  // it (used only if the sequence was not split)
+  f32x4 gt = {0.f, 0.f, 0.f, 0.f}, o1 = gt;
+  if (a.gate && grp == 0) {
+    gt = *reinterpret_cast<const f32x4*>(a.gate + (ob - a.out));
+    o1 = *reinterpret_cast<const f32x4*>(ob);
+  }
   const int* pre = a.ws_hdr;
   const int L = pre[a.B + 1 + b];
   if (L == 0) {
@@ -483,7 +491,14 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   auto wg_of = [&](int p) __attribute__((always_inline)) { return (int)((((long long)p + 1) * a.G - 1) / N); };
   const int w0 = wg_of(pb);
   const int np = wg_of(pe - 1) - w0 + 1;  // pieces
-  if (np == 1) return;  // finished inside one workgroup: the row is written
+  if (np == 1) {  // finished inside one workgroup: the row is written
+    if (a.gate && grp == 0) {  // in place: the decode kernel left the row ungated
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o1[e] *= sigmoidf(gt[e]);
+      *reinterpret_cast<f32x4*>(ob) = o1;
+    }
+    return;
+  }
   // slot of piece i, or -1 for an empty range
   auto slot_of = [&](int i) __attribute__((always_inline)) -> int {
     const int ww = w0 + i;
@@ -540,8 +555,7 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
       dd += f * s_den[gq][lane];
     }
     f32x4 o = n * (1.f / dd);
-    if (a.gate) {  // sigmoidGate epilogue
-      const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (ob - a.out));
+    if (a.gate) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
     }
@@ -569,7 +583,10 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   a.bt = block_table;
   a.seq_lens = seq_lens;
   a.out = (float*)out;
-  a.gate = gate;
+  // With a merge to follow, the merge applies the gate to every row: a gate
+  // load in the decode kernel's flush would wait (in-order vmcnt) for all the
+  // page loads it has in flight.
+  a.gate = num_splits > 1 ? nullptr : gate;
   a.ws_hdr = num_splits > 1 ? (int*)workspace : nullptr;
   a.ws = num_splits > 1 ? (float*)((char*)workspace + kGHeaderBytes) : nullptr;
   a.B = s.batch;
@@ -578,6 +595,7 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   hipLaunchKernelGGL(global_decode_kernel, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   if (num_splits <= 1) return DA_OK;  // nothing was split: no merge
+  a.gate = gate;
   // Expected pieces per sequence ~ G/B + 2: more pieces, more slot groups.
   const int est = num_splits / s.batch + 2;
   const unsigned nb = (unsigned)s.batch * (kGPair * kGMTiles);
