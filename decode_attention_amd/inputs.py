@@ -292,6 +292,49 @@ def make_global(seq_lens, *, Hkv=1, G=16, D=512, kv_dtype="bf16", tag=(200,),
 
 
 # ----------------------------------------------------------------------------
+# several queries per sequence (chunked prefill, speculative verification)
+# ----------------------------------------------------------------------------
+
+STREAM_MQ = 12
+
+
+@dataclass
+class MultiQueryWorkload:
+    kind: str                # "sliding" or "global"
+    q: np.ndarray            # [T, Hkv*G, D] stored; rows q_start[b]..q_start[b+1]-1 are sequence b's
+    q_start: np.ndarray      # int32 [B + 1]
+    base: object             # the SlidingWorkload / GlobalWorkload holding caches, table and seq_lens
+
+    @property
+    def max_queries(self):
+        return int(np.max(np.diff(self.q_start), initial=0))
+
+
+def make_multiquery(kind, seq_lens, q_counts, *, kv_dtype="bf16", tag=(800,), layer=0, P_max=None,
+                    q_scale=1.0, **shape):
+    """Caches as make_sliding / make_global build them, holding every
+    position some query can see, and q_counts[b] queries of sequence b at its
+    last q_counts[b] positions. ``shape``: Hkv, G, D (and window for
+    sliding)."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    q_counts = np.asarray(q_counts, dtype=np.int32)
+    q_start = np.concatenate([[0], np.cumsum(q_counts)]).astype(np.int32)
+    if kind == "sliding":
+        window = int(shape.pop("window", 1024))
+        # the earliest query, S - 1 positions before the last, looks back w - 1
+        fill_w = window + max(int(q_counts.max(initial=1)) - 1, 0) if window > 0 else 0
+        base = make_sliding(seq_lens, kv_dtype=kv_dtype, tag=tag, layer=layer, P_max=P_max,
+                            window=fill_w, **shape)
+        base.window = window
+    else:
+        base = make_global(seq_lens, kv_dtype=kv_dtype, tag=tag, layer=layer, P_max=P_max, **shape)
+    Hq = base.Hkv * base.G
+    w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), base.D)
+    q = rms_rows(rng_for(tag, layer, STREAM_MQ), (int(q_start[-1]), Hq, base.D), w_q) * np.float32(q_scale)
+    return MultiQueryWorkload(kind, to_storage(q, kv_dtype), q_start, base)
+
+
+# ----------------------------------------------------------------------------
 # decode-step inputs of the new token (before its norms and rotary embedding)
 # ----------------------------------------------------------------------------
 

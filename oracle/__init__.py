@@ -9,7 +9,8 @@ Sources (the pages are data; every formula here is restated, not pasted):
 
 * Op Specs page of google/gemma-4-12B, ``Attention.lean``: ``softmax`` (weights
   normalised over the visible positions only), ``causalGQA``, ``slidingGQA``,
-  ``decodeGQA``.
+  ``decodeGQA`` (the multi-query forms with several consecutive query
+  positions per sequence as well).
 * Op Specs overview page, "Attention" section and its NOTE on
   ``slidingDecodeGQA`` (decode over the last ``w`` cached positions; no Lean
   definition of its own, semantics from ``slidingGQA``).
@@ -43,6 +44,9 @@ from .paged import (  # noqa: F401
     sliding_visible_range,
     paged_decode_sliding,
     paged_decode_global,
+    multiquery_positions,
+    paged_multiquery_sliding,
+    paged_multiquery_global,
     f64_to_bf16_bits,
 )
 from .norm_rope import (  # noqa: F401

@@ -20,7 +20,7 @@ Stored values are decoded exactly to float64 (bf16 bit patterns are the top
 
 import numpy as np
 
-from .attention import decode_gqa, sliding_decode_gqa
+from .attention import causal_gqa, decode_gqa, sliding_decode_gqa, sliding_gqa
 
 PAGE = 16  # tokens per page (Model Spec page, "At a glance", shape domain)
 
@@ -125,6 +125,68 @@ def paged_decode_global(q, kv_cache, block_table, seq_lens, kv_dtype, scale=1.0)
         o = decode_gqa(scale, qf[b].reshape(Hkv, G, D), k, k)
         out[b] = o.reshape(Hq, D)
     return out
+
+
+def multiquery_positions(L, S):
+    """Positions of the S queries of a sequence whose cache holds L tokens,
+    the last S of which are the queries' own: query s sits at L - S + s, so
+    the last one is at L - 1 (chunked prefill and speculative verification,
+    ``causalGQA`` / ``slidingGQA`` with consecutive positions). A negative
+    position (S > L) has no cached key at or before it."""
+    return int(L) - int(S) + np.arange(int(S), dtype=np.int64)
+
+
+def _multiquery(q, q_start, seq_lens, kv_dtype, gather, window, scale):
+    """Shared front end: per sequence, the queries q[q_start[b]:q_start[b+1]]
+    at ``multiquery_positions``; keys gathered from the first position any
+    of them can see up to L - 1 (the others have weight exactly 0)."""
+    qf = stored_to_f64(q, kv_dtype)
+    T, Hq, D = qf.shape
+    q_start = np.asarray(q_start, dtype=np.int64)
+    out = np.zeros((T, Hq, D), dtype=np.float64)
+    for b in range(len(seq_lens)):
+        t0, t1 = int(q_start[b]), int(q_start[b + 1])
+        L, S = int(seq_lens[b]), t1 - t0
+        if S <= 0 or L <= 0:
+            continue
+        pos = multiquery_positions(L, S)
+        ok = pos >= 0
+        if not ok.any() or (window is not None and window <= 0):
+            continue
+        lo = 0 if window is None else max(0, int(pos[ok].min()) - int(window) + 1)
+        k, v = gather(b, np.arange(lo, L))
+        qb = qf[t0:t1][ok]
+        Hkv = k.shape[1]
+        qb = qb.reshape(len(qb), Hkv, Hq // Hkv, D)
+        rel = pos[ok] - lo  # positions within the gathered keys
+        if window is None:
+            o = causal_gqa(scale, rel, qb, k, v)
+        else:
+            o = sliding_gqa(scale, window, rel, qb, k, v)
+        out[t0:t1][ok] = o.reshape(len(qb), Hq, D)
+    return out
+
+
+def paged_multiquery_sliding(q, q_start, k_cache, v_cache, block_table, seq_lens, window,
+                             kv_dtype, scale=1.0):
+    """``slidingGQA`` of several queries per sequence over row-major paged
+    caches. q : [T, Hkv*G, D] stored, the queries of sequence b in rows
+    q_start[b] .. q_start[b+1]-1 at ``multiquery_positions``; returns float64
+    [T, Hkv*G, D] (0 for a query that sees no key)."""
+    def gather(b, pos):
+        k = stored_to_f64(gather_rowmajor_cache(k_cache, block_table[b], pos), kv_dtype)
+        v = stored_to_f64(gather_rowmajor_cache(v_cache, block_table[b], pos), kv_dtype)
+        return k, v
+    return _multiquery(q, q_start, seq_lens, kv_dtype, gather, int(window), scale)
+
+
+def paged_multiquery_global(q, q_start, kv_cache, block_table, seq_lens, kv_dtype, scale=1.0):
+    """``causalGQA`` of several queries per sequence over one tiled paged
+    cache read as both k and v (global layers)."""
+    def gather(b, pos):
+        k = stored_to_f64(gather_tiled_cache(kv_cache, block_table[b], pos), kv_dtype)
+        return k, k
+    return _multiquery(q, q_start, seq_lens, kv_dtype, gather, None, scale)
 
 
 def f64_to_bf16_bits(x):

@@ -163,3 +163,78 @@ def test_f64_to_bf16_rounding():
     ref_torch = torch.tensor(r).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(oracle.f64_to_bf16_bits(r.astype(np.float64)), ref_torch)
     np.testing.assert_array_equal(oracle.f64_to_bf16_bits(r.astype(np.float64)), I.f32_to_bf16_bits(r))
+
+
+# ---------------------------------------------------------------- several queries per sequence
+
+def test_multiquery_positions():
+    np.testing.assert_array_equal(P.multiquery_positions(10, 3), [7, 8, 9])
+    np.testing.assert_array_equal(P.multiquery_positions(2, 4), [-2, -1, 0, 1])
+    assert len(P.multiquery_positions(5, 0)) == 0
+
+
+def _truncated_decode(mq, b, s, pos):
+    """The decode oracle's output for query row s of sequence b over the same
+    caches with the length cut to pos + 1: a causal query at position pos sees
+    exactly what the decode query of a pos + 1 token sequence sees."""
+    base = mq.base
+    q = mq.q[s][None]
+    bt = base.block_table[b][None]
+    sl = np.array([pos + 1], dtype=np.int32)
+    if mq.kind == "sliding":
+        return P.paged_decode_sliding(q, base.k_cache, base.v_cache, bt, sl, base.window, base.kv_dtype)[0]
+    return P.paged_decode_global(q, base.kv_cache, bt, sl, base.kv_dtype)[0]
+
+
+@pytest.mark.parametrize("kind", ["sliding", "global"])
+def test_multiquery_rows_equal_truncated_decode(kind):
+    # Small heads so the decode oracle runs fast; the q counts include 0, 1,
+    # more queries than cached tokens, and chunks crossing window and page
+    # boundaries.
+    shape = dict(Hkv=2, G=2, D=16, window=20) if kind == "sliding" else dict(Hkv=1, G=4, D=32)
+    seq_lens = [5, 40, 17, 3, 64, 33]
+    counts = [0, 1, 7, 5, 30, 16]
+    mq = I.make_multiquery(kind, seq_lens, counts, kv_dtype="bf16", tag=(31, len(kind)), **shape)
+    got = (P.paged_multiquery_sliding(mq.q, mq.q_start, mq.base.k_cache, mq.base.v_cache, mq.base.block_table,
+                                      mq.base.seq_lens, mq.base.window, "bf16") if kind == "sliding" else
+           P.paged_multiquery_global(mq.q, mq.q_start, mq.base.kv_cache, mq.base.block_table, mq.base.seq_lens,
+                                     "bf16"))
+    assert np.isfinite(got).all()
+    for b, (L, S) in enumerate(zip(seq_lens, counts)):
+        for j in range(S):
+            s, pos = int(mq.q_start[b]) + j, L - S + j  # the last query sits at L - 1
+            if pos < 0:
+                assert np.all(got[s] == 0)
+            else:
+                np.testing.assert_allclose(got[s], _truncated_decode(mq, b, s, pos), rtol=1e-12, atol=1e-13)
+        if S > 0:  # the last query is the decode query of the untouched sequence
+            base = mq.base
+            s = int(mq.q_start[b]) + S - 1
+            q, bt, sl = mq.q[s][None], base.block_table[b][None], base.seq_lens[b:b + 1]
+            ref = (P.paged_decode_sliding(q, base.k_cache, base.v_cache, bt, sl, base.window, "bf16")
+                   if kind == "sliding" else P.paged_decode_global(q, base.kv_cache, bt, sl, "bf16"))
+            np.testing.assert_allclose(got[s], ref[0], rtol=1e-12, atol=1e-13)
+
+
+def test_multiquery_sliding_brute_force():
+    # Literal per-(query, head, key) loop over the slidingGQA predicate with
+    # exp and no max-subtraction, on the gathered logical rows.
+    import math
+    mq = I.make_multiquery("sliding", [12, 30], [4, 9], kv_dtype="f32", tag=(32,), Hkv=1, G=2, D=4, window=6,
+                           q_scale=0.3)
+    base = mq.base
+    got = P.paged_multiquery_sliding(mq.q, mq.q_start, base.k_cache, base.v_cache, base.block_table,
+                                     base.seq_lens, 6, "f32")
+    for b, (L, S) in enumerate(zip([12, 30], [4, 9])):
+        for j, p in enumerate(range(L - S, L)):
+            s = int(mq.q_start[b]) + j
+            lo = max(0, p - 5)
+            keys = P.gather_rowmajor_cache(base.k_cache, base.block_table[b], np.arange(lo, p + 1)).astype(float)
+            vals = P.gather_rowmajor_cache(base.v_cache, base.block_table[b], np.arange(lo, p + 1)).astype(float)
+            for h in range(2):
+                qv = mq.q[s, h].astype(float)
+                e = [math.exp(sum(qv[d] * keys[l, 0, d] for d in range(4))) for l in range(len(keys))]
+                z = sum(e)
+                for d in range(4):
+                    want = sum(e[l] * vals[l, 0, d] for l in range(len(keys))) / z
+                    assert abs(got[s, h, d] - want) < 1e-12
