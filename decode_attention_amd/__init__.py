@@ -14,6 +14,9 @@ from .binding import (  # noqa: F401
     attn_decode_global_gated,
     attn_kv_append_sliding,
     attn_kv_append_global,
+    attn_multiquery_sliding,
+    attn_multiquery_global,
+    attn_multiquery_workspace_bytes,
     attn_status_string,
     library_path,
     load_library,

@@ -45,7 +45,9 @@ class DaShape(ctypes.Structure):
 
 EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
            "attn_decode_sliding_gated", "attn_decode_global_gated",
-           "attn_kv_append_sliding", "attn_kv_append_global", "attn_status_string")
+           "attn_kv_append_sliding", "attn_kv_append_global",
+           "attn_multiquery_sliding", "attn_multiquery_global", "attn_multiquery_workspace_bytes",
+           "attn_status_string")
 
 
 def library_path():
@@ -83,6 +85,15 @@ def load_library():
         lib.attn_kv_append_sliding.restype = ctypes.c_int32
         lib.attn_kv_append_global.argtypes = [vp] * 8 + [ctypes.POINTER(DaShape), vp]
         lib.attn_kv_append_global.restype = ctypes.c_int32
+        lib.attn_multiquery_sliding.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_int32, vp,
+                                                ctypes.POINTER(DaShape), vp, ctypes.c_size_t, vp]
+        lib.attn_multiquery_sliding.restype = ctypes.c_int32
+        lib.attn_multiquery_global.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
+                                               ctypes.c_size_t, vp]
+        lib.attn_multiquery_global.restype = ctypes.c_int32
+        lib.attn_multiquery_workspace_bytes.argtypes = [ctypes.POINTER(DaShape), ctypes.c_int32, ctypes.c_int32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]
+        lib.attn_multiquery_workspace_bytes.restype = ctypes.c_int32
         lib.attn_status_string.argtypes = [ctypes.c_int32]
         lib.attn_status_string.restype = ctypes.c_char_p
         del i32p
@@ -325,3 +336,91 @@ def attn_kv_append_global(q_raw, kv_raw, w_q, w_k, block_table, positions, kv_ca
                                      _ptr(positions), _ptr(kv_cache), _ptr(q_out), ctypes.byref(shape),
                                      _stream(stream)))
     return q_out
+
+
+def attn_multiquery_workspace_bytes(shape, max_queries, window=0):
+    n = ctypes.c_size_t(0)
+    _check(load_library().attn_multiquery_workspace_bytes(ctypes.byref(shape), int(max_queries), int(window),
+                                                          ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(device, st, need):
+    import torch
+    key = (device, st.value, need)
+    ws = _workspaces.get(key)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _multiquery(sliding, q, q_start, max_queries, caches, block_table, seq_lens, window, out, workspace,
+                num_splits, stream):
+    import torch
+    lib = load_library()
+    _require(q.is_cuda and q.dim() == 3 and q.is_contiguous() and q.dtype == torch.bfloat16,
+             "q must be a contiguous bf16 cuda [T, Hq, D] tensor")
+    for c in caches:
+        _require(c.is_cuda and c.is_contiguous() and c.device == q.device and c.dtype == q.dtype,
+                 "caches must be contiguous bf16, on q's device")
+    B = seq_lens.shape[0]
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+             and block_table.device == q.device and block_table.shape[0] == B,
+             "block_table must be contiguous int32 [B, P_max] on q's device")
+    _require(seq_lens.dtype == torch.int32 and seq_lens.dim() == 1 and seq_lens.is_contiguous()
+             and seq_lens.device == q.device, "seq_lens must be contiguous int32 [B] on q's device")
+    _require(q_start.dtype == torch.int32 and q_start.dim() == 1 and q_start.is_contiguous()
+             and q_start.device == q.device and q_start.shape[0] == B + 1,
+             "q_start must be contiguous int32 [B + 1] on q's device")
+    T, Hq, D = q.shape
+    if sliding:
+        k_cache = caches[0]
+        _require(k_cache.dim() == 4 and k_cache.shape == caches[1].shape and k_cache.shape[2] == PAGE_SIZE,
+                 "k_cache/v_cache must be [P, Hkv, 16, D]")
+        P, Hkv, _, Dk = k_cache.shape
+        _require(Dk == D and Hq % Hkv == 0, "head shape mismatch")
+    else:
+        kv = caches[0]
+        _require(kv.dim() == 5 and kv.shape[3] == PAGE_SIZE, "kv_cache must be tiled [P, Hkv, D/x, 16, x]")
+        P, Hkv, nx, _, x = kv.shape
+        _require(nx * x == D and Hq % Hkv == 0, "head shape mismatch")
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), num_splits)
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (T, Hq, D),
+             "out must be contiguous fp32 [T, Hq, D]")
+    st = _stream(stream)
+    need = attn_multiquery_workspace_bytes(shape, max_queries, window)
+    if workspace is None and need > 0:
+        workspace = _workspace(q.device, st, need)
+    ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if sliding:
+        _check(lib.attn_multiquery_sliding(_ptr(q), _ptr(q_start), int(max_queries), _ptr(caches[0]),
+                                           _ptr(caches[1]), _ptr(block_table), _ptr(seq_lens), int(window),
+                                           _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st))
+    else:
+        _check(lib.attn_multiquery_global(_ptr(q), _ptr(q_start), int(max_queries), _ptr(caches[0]),
+                                          _ptr(block_table), _ptr(seq_lens), _ptr(out), ctypes.byref(shape),
+                                          ws_ptr, ws_bytes, st))
+    return out
+
+
+def attn_multiquery_sliding(q, q_start, max_queries, k_cache, v_cache, block_table, seq_lens, window, out=None,
+                            workspace=None, num_splits=0, stream=None):
+    """slidingGQA for several queries per sequence at its last positions:
+    q bf16 [T, Hq, 256] (sequence b's rows q_start[b]..q_start[b+1]-1,
+    query s at position L - S_b + s); k_cache, v_cache [P, Hkv, 16, 256];
+    returns out fp32 [T, Hq, 256]. max_queries >= every S_b."""
+    return _multiquery(True, q, q_start, max_queries, (k_cache, v_cache), block_table, seq_lens, window, out,
+                       workspace, num_splits, stream)
+
+
+def attn_multiquery_global(q, q_start, max_queries, kv_cache, block_table, seq_lens, out=None, workspace=None,
+                           num_splits=0, stream=None):
+    """causalGQA for several queries per sequence at its last positions, with
+    values = keys: q bf16 [T, 16, 512], kv_cache tiled [P, 1, 64, 16, 8];
+    returns out fp32 [T, 16, 512]."""
+    return _multiquery(False, q, q_start, max_queries, (kv_cache,), block_table, seq_lens, 0, out, workspace,
+                       num_splits, stream)

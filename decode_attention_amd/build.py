@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.cpp", "sliding.hip", "global.hip", "append.hip"]
+SOURCES = ["api.cpp", "sliding.hip", "global.hip", "append.hip", "multiquery.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code.

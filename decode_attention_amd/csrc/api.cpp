@@ -100,9 +100,73 @@ da_status decode_global(const void* q, const void* kv_cache, const int32_t* bloc
                            (hipStream_t)stream);
 }
 
+constexpr int kMaxQueries = 1 << 18;  // the model's position domain
+
+// Shapes the multi-query kernels are built for: sliding (any Hkv, G 2, D 256)
+// or global (Hkv 1, G 16, D 512), bf16 caches.
+da_status check_multiquery_shape(const da_shape* s, bool sliding, int32_t max_queries) {
+  da_status st = check_common(s);
+  if (st != DA_OK) return st;
+  if (max_queries <= 0) return DA_ERR_INVALID_ARG;
+  if (max_queries > kMaxQueries) return DA_ERR_UNSUPPORTED;
+  if (s->kv_dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;
+  if (sliding ? (s->group != 2 || s->head_dim != 256) : (s->num_kv_heads != 1 || s->group != 16 || s->head_dim != 512))
+    return DA_ERR_UNSUPPORTED;
+  if ((long long)s->batch * s->num_kv_heads > 65535 || s->num_splits > 65535) return DA_ERR_UNSUPPORTED;
+  return DA_OK;
+}
+
+da_status multiquery(bool sliding, const void* q, const int32_t* q_start, int32_t max_queries, const void* k_cache,
+                     const void* v_cache, const int32_t* block_table, const int32_t* seq_lens, int32_t window,
+                     void* out, const da_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  da_status st = check_multiquery_shape(shape, sliding, max_queries);
+  if (st != DA_OK) return st;
+  if (!q || !q_start || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
+  if (window < 0) return DA_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  const int splits = da::multiquery_num_splits(*shape, max_queries, window, cus);
+  const size_t need = da::multiquery_workspace_bytes(*shape, max_queries, splits);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
+  return da::launch_multiquery(q, q_start, max_queries, k_cache, v_cache, block_table, seq_lens, window, out,
+                               *shape, splits, workspace, (hipStream_t)stream);
+}
+
 }  // namespace
 
 extern "C" {
+
+da_status attn_multiquery_sliding(const void* q, const int32_t* q_start, int32_t max_queries,
+                                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t window, void* out, const da_shape* shape,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return multiquery(true, q, q_start, max_queries, k_cache, v_cache, block_table, seq_lens, window, out, shape,
+                    workspace, workspace_bytes, stream);
+}
+
+da_status attn_multiquery_global(const void* q, const int32_t* q_start, int32_t max_queries,
+                                 const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
+                                 void* out, const da_shape* shape, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return multiquery(false, q, q_start, max_queries, kv_cache, kv_cache, block_table, seq_lens, 0, out, shape,
+                    workspace, workspace_bytes, stream);
+}
+
+da_status attn_multiquery_workspace_bytes(const da_shape* shape, int32_t max_queries, int32_t window,
+                                          size_t* bytes) {
+  if (!bytes) return DA_ERR_INVALID_ARG;
+  const bool sliding = shape && shape->head_dim == 256;
+  da_status st = check_multiquery_shape(shape, sliding, max_queries);
+  if (st != DA_OK) return st;
+  if (window < 0) return DA_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  *bytes = da::multiquery_workspace_bytes(*shape, max_queries,
+                                          da::multiquery_num_splits(*shape, max_queries, window, cus));
+  return DA_OK;
+}
 
 da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, const int32_t* seq_lens, int32_t window,

@@ -31,4 +31,12 @@ da_status launch_append_global(const float* q_raw, const float* kv_raw, const fl
                                const int32_t* block_table, const int32_t* positions, void* kv_cache, void* q_out,
                                const da_shape& s, hipStream_t stream);
 
+// Several queries per sequence at its last positions (row f2).
+int multiquery_num_splits(const da_shape& s, int max_queries, int window, int num_cus);
+size_t multiquery_workspace_bytes(const da_shape& s, int max_queries, int num_splits);
+da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queries, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                            int window, void* out, const da_shape& s, int num_splits, void* workspace,
+                            hipStream_t stream);
+
 }  // namespace da

@@ -1,0 +1,399 @@
+// Paged attention of several queries per sequence (chunked prefill,
+// speculative verification): the S queries of a sequence with L cached
+// tokens sit at positions L - S .. L - 1 (their own keys are already in the
+// cache) and each sees the keys l <= its position p; on sliding layers only
+// those with p - w < l.
+//
+// Pages: Op Specs of google/gemma-4-12B, Attention.lean (causalGQA,
+// slidingGQA); gemma-4-12b Model Spec, the attn.core rows of the sliding and
+// global layers (head map h / G, scale 1, values = keys on global layers).
+//
+// Rows. A query row is one (query, head) pair of one KV head: on sliding
+// layers its G = 2 heads, on global layers the 16 heads of the single KV head.
+// A workgroup takes a block of rows of one (sequence, KV head) with 8 waves of
+// 16 rows x 256 coordinates; with D = 512 two waves share 16 rows, one per
+// coordinate half, and add their partial scores through LDS in a fixed
+// order. Sliding: 128 rows (64 queries) per workgroup; global: 64 rows (4).
+//
+// Keys. The workgroup walks the pages that some row of its block can see,
+// two pages per step, staged in LDS (double-buffered), with the loads of the
+// next two steps held in registers. Per step and wave:
+//   S^T (16 tokens x 16 rows) = K Q^T: 8 mfma_f32_16x16x32_bf16 per page, K
+//     read from LDS in the A-operand layout, Q^T kept in registers;
+//   per-row masks (l <= p, and l > p - w on sliding layers), online softmax
+//     in base 2 with lazy rescaling;
+//   O^T (256 x 16) += V^T P^T: one mfma_f32_16x16x32_bf16 per 16-coordinate
+//     tile, its 32-wide k dimension holding the 16 tokens of each page; V^T
+//     read transposed from LDS with ds_read_b64_tr_b16.
+// P enters the product rounded to bf16 and the denominator sums the same
+// rounded values, so every output is a weighted average whose weights are
+// exact to about 2^-9 relative.
+//
+// Split over keys. When sequences x KV heads x row blocks gives too few
+// workgroups for the chip, each block's pages are divided among nsplit
+// workgroups that write partial (acc, m, l) per row, and mq_merge_kernel
+// combines them: M = max m_i, o = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace da {
+
+constexpr int kMWaves = 8;
+constexpr int kMThreads = kMWaves * kWave;
+constexpr int kMSlice = 256;                 // coordinates per wave
+constexpr int kMKSteps = kMSlice / 32;       // 16x16x32 k-steps per page and wave
+constexpr int kMTiles = kMSlice / 16;        // 16-coordinate output tiles per wave
+constexpr int kMRegion = 16384;              // LDS bytes per region of a step (2 pages of K, or of V)
+constexpr float kMRescale = 32.f;            // lazy-rescale threshold, log2 units
+
+struct MQArgs {
+  const uint16_t* q;        // [T][Hq][D] bf16 bits; sequence b's rows from q_start[b]
+  const uint16_t* k;        // sliding [P][Hkv][16][256]; global tiled [P][1][64][16][8]
+  const uint16_t* v;        // sliding [P][Hkv][16][256]; global: the same as k
+  const int32_t* bt;        // [B][P_max]
+  const int32_t* seq_lens;  // [B]
+  const int32_t* q_start;   // [B + 1]
+  float* out;               // [T][Hq][D]
+  float* ws;                // partial slots, [B*Hkv][nblk][nsplit][slot] (nsplit > 1)
+  int B, Hkv, P_max, window, nblk, nsplit;
+};
+
+template <int D, int G>
+struct MQShape {
+  static_assert((D == 256 && G == 2) || (D == 512 && G == 16), "built shapes");
+  static constexpr bool kSliding = D == 256;
+  static constexpr int kHalves = D / kMSlice;           // waves per 16-row block
+  static constexpr int kRows = 16 * kMWaves / kHalves;  // rows per workgroup
+  static constexpr int kQueries = kRows / G;            // queries per workgroup
+  static constexpr int kKPage = kSliding ? 8192 : 16384;  // LDS bytes per page of K (and of V)
+  static constexpr int kVBase = kSliding ? kMRegion : 0;  // V region (global: V = K)
+  static constexpr int kSlotFloats = kRows * D + 2 * kRows;
+};
+
+__device__ __forceinline__ int mq_rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int D, int G>
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) void mq_kernel(MQArgs a) {
+  using C = MQShape<D, G>;
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][2 * kMRegion];
+  __shared__ f32x4 s_part[2][kMWaves][kWave];  // partial S^T per page (D = 512)
+
+  const int blk = blockIdx.x, split = blockIdx.y, bc = blockIdx.z;
+  const int b = bc / a.Hkv, c = bc - b * a.Hkv;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
+  const int q0 = a.q_start[b];
+  const int S = a.q_start[b + 1] - q0;
+  const int s0 = blk * C::kQueries;
+  if (s0 >= S) return;  // no rows in this block (the merge skips it too)
+  const int s1 = min(S, s0 + C::kQueries) - 1;
+  const int p0 = L - S + s0, p1 = L - S + s1;  // positions of the block's first and last query
+  // Keys some row of the block sees: [klo, khi].
+  const int klo = C::kSliding ? max(0, p0 - a.window + 1) : 0;
+  const int khi = p1;
+  const bool any = khi >= 0 && (!C::kSliding || a.window > 0);
+  const int jlo = any ? klo / kPage : 0;
+  const int np = any ? khi / kPage - jlo + 1 : 0;
+  const int ja = jlo + (int)((long long)split * np / a.nsplit);
+  const int jb = jlo + (int)((long long)(split + 1) * np / a.nsplit);
+  const int nsteps = (jb - ja + 1) / 2;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = mq_rfl(tid / kWave);
+  const int rb = wv / C::kHalves, hf = wv % C::kHalves;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int r_wg = rb * 16 + n;  // this lane's row within the workgroup
+  const int s_r = s0 + r_wg / G;
+  const int head = c * G + r_wg % G;
+  const bool valid = s_r <= s1;
+  const int pos_r = valid ? L - S + s_r : -1;  // -1: sees nothing
+  const int lo_r = C::kSliding ? max(0, pos_r - a.window + 1) : 0;
+  const int Hq = a.Hkv * G;
+
+  // Q^T B operands: row n, coordinates 256 hf + 32 i + 8 g4 .. +8.
+  uint4 qv[kMKSteps];
+  {
+    const uint16_t* qp = a.q + ((size_t)(q0 + s_r) * Hq + head) * D + hf * kMSlice + 8 * g4;
+#pragma unroll
+    for (int i = 0; i < kMKSteps; ++i) qv[i] = valid ? ld16(qp + 32 * i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Chunk u (0..3) of 16 bytes per step and thread. Sliding: u = 2 * (V) +
+  // page; the row-major slab [16 tokens][256] is stored as [32 chunks][16
+  // tokens][8], thread tid taking chunk tid >> 4 of token tid & 15. Global:
+  // the tiled page [64 chunks][16 tokens][8] is copied as it is, chunk
+  // (u & 1) * 512 + tid of page u >> 1.
+  const int c_tok = tid & 15;
+  const int c_src = C::kSliding ? (tid & 15) * 256 + (tid >> 4) * 8 : tid * 8;  // + u-dependent part
+  const int c_lds = C::kSliding ? ((tid >> 4) * 16 + (tid & 15)) * 16 : tid * 16;
+  auto u_pg = [](int u) constexpr { return C::kSliding ? (u & 1) : (u >> 1); };
+  auto u_src = [](int u) constexpr { return C::kSliding ? 0 : (u & 1) * kMThreads * 8; };
+  auto u_lds = [](int u) constexpr {
+    return C::kSliding ? (u >> 1) * kMRegion + (u & 1) * C::kKPage : (u >> 1) * C::kKPage + (u & 1) * kMThreads * 16;
+  };
+  const size_t slab = (size_t)kPage * D;
+  auto load_step = [&](int k, uint4(&r)[4]) __attribute__((always_inline)) {
+    const int j0 = ja + 2 * k;
+    int ph[2] = {0, 0};
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+      if (j0 + pg < jb) ph[pg] = a.bt[(size_t)b * a.P_max + j0 + pg];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      r[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (j0 + u_pg(u) < jb) {
+        const uint16_t* src = (C::kSliding && u >= 2) ? a.v : a.k;
+        r[u] = ld16(src + ((size_t)ph[u_pg(u)] * a.Hkv + c) * slab + c_src + u_src(u));
+      }
+    }
+  };
+  // Tokens no row of the block sees (and pages of other splits) are stored
+  // as zeros, so that whatever that storage holds, NaN included, meets only
+  // zero weights.
+  auto store_step = [&](int k, const uint4(&r)[4], int buf) __attribute__((always_inline)) {
+    const int j0 = ja + 2 * k;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u_pg(u), pos = j * kPage + c_tok;
+      const bool keep = j < jb && pos >= klo && pos <= khi;
+      *reinterpret_cast<uint4*>(&s_kv[buf][c_lds + u_lds(u)]) = keep ? r[u] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+
+  f32x4 acc[kMTiles];
+#pragma unroll
+  for (int t = 0; t < kMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int s16 = lane & 15;
+  const int tr_off = ((s16 & 3) >> 1) * 256 + (4 * g4 + (s16 >> 2)) * 16 + (s16 & 1) * 8;
+
+  auto compute = [&](int k, int buf) __attribute__((always_inline)) {
+    const int j0 = ja + 2 * k;
+    f32x4 sp[2];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const uint8_t* kp = &s_kv[buf][pg * C::kKPage + hf * 8192 + lane * 16];
+      f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      constexpr int kKB = 4;  // k-steps per batch of LDS reads
+#pragma unroll
+      for (int i0 = 0; i0 < kMKSteps; i0 += kKB) {
+        uint4 kv4[kKB];
+#pragma unroll
+        for (int i = 0; i < kKB; ++i) kv4[i] = *reinterpret_cast<const uint4*>(kp + (i0 + i) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kKB; ++i)
+          x[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv4[i]),
+                                                             __builtin_bit_cast(bf16x8, qv[i0 + i]), x[i & 1], 0, 0, 0);
+      }
+      sp[pg] = x[0] + x[1];
+    }
+    if constexpr (C::kHalves == 2) {  // add the two coordinate halves, same order in both waves
+      s_part[0][wv][lane] = sp[0];
+      s_part[1][wv][lane] = sp[1];
+      __syncthreads();
+      sp[0] = s_part[0][wv & ~1][lane] + s_part[0][wv | 1][lane];
+      sp[1] = s_part[1][wv & ~1][lane] + s_part[1][wv | 1][lane];
+    }
+    float sc[8];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + pg, pos = j * kPage + 4 * g4 + e;
+        const bool vis = j < jb && pos >= lo_r && pos <= pos_r;
+        sc[4 * pg + e] = vis ? sp[pg][e] * kLog2e : -INFINITY;
+      }
+    // Lazy rescaling (as in the decode kernels): the reference m_run moves
+    // only when a score exceeds it by more than kMRescale.
+    float lmax = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sc[e]);
+    if (__any(lmax > m_run + kMRescale)) {
+      float mp = fmaxf(lmax, xor16(lmax));
+      mp = fmaxf(mp, xor32(mp));  // row max over the 4 lane groups of the row
+      const float m_new = (mp > m_run + kMRescale) ? mp : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);  // 0 from -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < kMTiles; ++t) acc[t] *= alpha;
+    }
+    // P^T operand: k-slots 8 g4 + e hold page 0's token 4 g4 + e, slots
+    // 8 g4 + 4 + e page 1's; the V^T operand is built the same way.
+    bf16x8 pp;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pv = (sc[e] == -INFINITY) ? 0.f : exp2_fast(sc[e] - m_run);
+      pp[e] = (__bf16)pv;
+      l_run += (float)pp[e];
+    }
+    const uint8_t* vb = &s_kv[buf][C::kVBase + hf * 8192];
+    constexpr int kVB = 4;  // tiles per batch of transposed reads
+#pragma unroll
+    for (int t0 = 0; t0 < kMTiles; t0 += kVB) {
+      s16x4 v0[kVB], v1[kVB];
+#pragma unroll
+      for (int u = 0; u < kVB; ++u) {
+        v0[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) uint8_t*)vb +
+                                                       (t0 + u) * 512 + tr_off));
+        v1[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) uint8_t*)vb +
+                                                       C::kKPage + (t0 + u) * 512 + tr_off));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kVB; ++u) {
+        const bf16x8 vt = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0[u], v1[u], 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[t0 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pp, acc[t0 + u], 0, 0, 0);
+      }
+    }
+  };
+
+  if (nsteps > 0) {
+    uint4 ra[4], rb2[4];
+    load_step(0, ra);
+    load_step(1, rb2);
+    store_step(0, ra, 0);
+    load_step(2, ra);
+    __syncthreads();
+    // Step k computes from buffer k % 2 while the registers hold steps k + 1
+    // and k + 2; loads past the last step are predicated off (zeros).
+    for (int k = 0; k < nsteps; k += 2) {
+      compute(k, 0);
+      store_step(k + 1, rb2, 1);
+      load_step(k + 3, rb2);
+      __syncthreads();
+      if (k + 1 >= nsteps) break;
+      compute(k + 1, 1);
+      store_step(k + 2, ra, 0);
+      load_step(k + 4, ra);
+      __syncthreads();
+    }
+  }
+
+  float lt = l_run + xor16(l_run);
+  lt += xor32(lt);  // the row's denominator (its 4 lane groups)
+  if (a.nsplit == 1) {
+    if (valid) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;  // nothing visible: 0
+      float* op = a.out + ((size_t)(q0 + s_r) * Hq + head) * D + hf * kMSlice + 4 * g4;
+#pragma unroll
+      for (int t = 0; t < kMTiles; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = acc[t] * inv;
+    }
+  } else {
+    float* slot = a.ws + ((size_t)(bc * a.nblk + blk) * a.nsplit + split) * C::kSlotFloats;
+    float* ap = slot + (size_t)r_wg * D + hf * kMSlice + 4 * g4;
+#pragma unroll
+    for (int t = 0; t < kMTiles; ++t) *reinterpret_cast<f32x4*>(ap + 16 * t) = acc[t];
+    if (g4 == 0 && hf == 0) {
+      slot[C::kRows * D + r_wg] = m_run;
+      slot[C::kRows * D + C::kRows + r_wg] = lt;
+    }
+  }
+}
+
+// Combines the nsplit partial slots of one row block: thread item = (row,
+// 4 coordinates), consecutive threads on consecutive coordinates.
+template <int D, int G>
+__global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
+  using C = MQShape<D, G>;
+  const int blk = blockIdx.x, bc = blockIdx.z;
+  const int b = bc / a.Hkv, c = bc - b * a.Hkv;
+  const int q0 = a.q_start[b];
+  const int S = a.q_start[b + 1] - q0;
+  const int s0 = blk * C::kQueries;
+  if (s0 >= S) return;
+  const float* base = a.ws + (size_t)(bc * a.nblk + blk) * a.nsplit * C::kSlotFloats;
+  const int Hq = a.Hkv * G;
+  for (int it = threadIdx.x; it < C::kRows * D / 4; it += 256) {
+    const int r = it / (D / 4), d = (it - r * (D / 4)) * 4;
+    const int s_r = s0 + r / G;
+    if (s_r >= S) continue;
+    float M = -INFINITY;
+    for (int k = 0; k < a.nsplit; ++k) M = fmaxf(M, base[(size_t)k * C::kSlotFloats + C::kRows * D + r]);
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < a.nsplit; ++k) {
+        const float* sl = base + (size_t)k * C::kSlotFloats;
+        const float mk = sl[C::kRows * D + r];
+        if (mk == -INFINITY) continue;  // no key in this piece
+        const float f = exp2_fast(mk - M);
+        num += f * *reinterpret_cast<const f32x4*>(sl + (size_t)r * D + d);
+        den += f * sl[C::kRows * D + C::kRows + r];
+      }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    float* op = a.out + ((size_t)(q0 + s_r) * Hq + c * G + r % G) * D + d;
+    *reinterpret_cast<f32x4*>(op) = num * inv;
+  }
+}
+
+template <int D, int G>
+static int mq_blocks(int max_queries) {
+  return (max_queries + MQShape<D, G>::kQueries - 1) / MQShape<D, G>::kQueries;
+}
+
+int multiquery_num_splits(const da_shape& s, int max_queries, int window, int num_cus) {
+  if (s.num_splits > 0) return s.num_splits;
+  const bool sliding = s.head_dim == 256;
+  const int nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
+  const long long base = (long long)s.batch * s.num_kv_heads * nblk;
+  // pages a block can need: the window plus the block's queries, or the row
+  const int qpb = sliding ? MQShape<256, 2>::kQueries : MQShape<512, 16>::kQueries;
+  const long long span = sliding ? std::min<long long>(s.max_pages_per_seq, (window + qpb - 1) / kPage + 2)
+                                 : s.max_pages_per_seq;
+  long long want = (2LL * num_cus + base - 1) / base;  // about two workgroups per compute unit
+  const long long cap = std::max<long long>(1, span / 8);  // at least ~4 steps per piece
+  want = std::min(want, cap);
+  return (int)std::max<long long>(1, want);
+}
+
+size_t multiquery_workspace_bytes(const da_shape& s, int max_queries, int num_splits) {
+  if (num_splits <= 1) return 0;
+  const bool sliding = s.head_dim == 256;
+  const int nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
+  const size_t slot = sliding ? MQShape<256, 2>::kSlotFloats : MQShape<512, 16>::kSlotFloats;
+  return (size_t)s.batch * s.num_kv_heads * nblk * (size_t)num_splits * slot * sizeof(float);
+}
+
+da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queries, const void* k_cache,
+                            const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                            int window, void* out, const da_shape& s, int num_splits, void* workspace,
+                            hipStream_t stream) {
+  MQArgs a;
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k_cache;
+  a.v = (const uint16_t*)v_cache;
+  a.bt = block_table;
+  a.seq_lens = seq_lens;
+  a.q_start = q_start;
+  a.out = (float*)out;
+  a.ws = num_splits > 1 ? (float*)workspace : nullptr;
+  a.B = s.batch;
+  a.Hkv = s.num_kv_heads;
+  a.P_max = s.max_pages_per_seq;
+  a.window = window;
+  a.nsplit = num_splits;
+  const bool sliding = s.head_dim == 256;
+  a.nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
+  const dim3 grid((unsigned)a.nblk, (unsigned)num_splits, (unsigned)(s.batch * s.num_kv_heads));
+  if (sliding)
+    hipLaunchKernelGGL((mq_kernel<256, 2>), grid, dim3(kMThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mq_kernel<512, 16>), grid, dim3(kMThreads), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
+  if (num_splits <= 1) return DA_OK;
+  const dim3 mgrid((unsigned)a.nblk, 1, (unsigned)(s.batch * s.num_kv_heads));
+  if (sliding)
+    hipLaunchKernelGGL((mq_merge_kernel<256, 2>), mgrid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mq_merge_kernel<512, 16>), mgrid, dim3(256), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
+}
+
+}  // namespace da

@@ -206,6 +206,52 @@ da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const f
                                 void* kv_cache, void* q_out, const da_shape* shape, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
+/*
+ * Several queries per sequence (chunked prefill, speculative verification):
+ * causalGQA and slidingGQA of the Op Specs (Attention.lean) with consecutive
+ * query positions. Sequence b holds L = seq_lens[b] cached tokens, the last
+ * S_b = q_start[b+1] - q_start[b] of which are its queries' own (written to
+ * the cache before the call, e.g. by attn_kv_append_*); query s of sequence b
+ * (q row q_start[b] + s) sits at position p = L - S_b + s and sees the keys
+ * l <= p, and on sliding layers only those with p - window < l. A query with
+ * p < 0 (S_b > L), or that sees no key, gets an all-zero output row.
+ *
+ *   q       : [T][Hkv*G][D] bf16, T = q_start[batch]; the rows of sequence b
+ *             are q_start[b] .. q_start[b+1]-1.
+ *   q_start : int32 [batch + 1] device array, q_start[0] = 0, non-decreasing.
+ *   max_queries : host int, >= every S_b (sizes the grid; rows of a sequence
+ *             past max_queries are not written). 1 .. 2^18.
+ *   caches, block_table, seq_lens : as for the decode calls (sliding:
+ *             k_cache, v_cache row-major; global: kv_cache tiled, read as
+ *             both k and v). The block-table entries read are those of the
+ *             positions some query sees.
+ *   out     : [T][Hkv*G][D] fp32.
+ *   workspace : device buffer of at least attn_multiquery_workspace_bytes()
+ *             bytes for the same shape, max_queries and window (0 bytes when
+ *             the call needs none; may then be NULL). It holds per-piece
+ *             partial results when a block's keys are split over several
+ *             workgroups; no initialisation needed. Calls that share a
+ *             workspace must be ordered (same stream).
+ *
+ * Built shapes: sliding (Hkv any, G = 2, D = 256), global (Hkv = 1, G = 16,
+ * D = 512); bf16 caches only; batch * Hkv <= 65535. shape->num_splits > 0
+ * forces the number of pieces per block (tests); 0 chooses it.
+ */
+da_status attn_multiquery_sliding(const void* q, const int32_t* q_start, int32_t max_queries,
+                                  const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                  const int32_t* seq_lens, int32_t window, void* out,
+                                  const da_shape* shape, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+da_status attn_multiquery_global(const void* q, const int32_t* q_start, int32_t max_queries,
+                                 const void* kv_cache, const int32_t* block_table,
+                                 const int32_t* seq_lens, void* out, const da_shape* shape,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+/* Workspace size of the multi-query call for this shape (head_dim 256:
+ * sliding, 512: global), max_queries and window (ignored for global). Needs a
+ * current gfx950 device (the split depends on its compute-unit count). */
+da_status attn_multiquery_workspace_bytes(const da_shape* shape, int32_t max_queries, int32_t window,
+                                          size_t* bytes);
+
 const char* attn_status_string(da_status status);
 
 #ifdef __cplusplus

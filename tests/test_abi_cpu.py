@@ -166,3 +166,34 @@ def test_gated_validation(lib):
 def test_gated_no_device_reported_after_valid_arguments(lib):
     assert sliding_gated(lib, _shape()) == -4
     assert global_gated(lib, _gshape()) == -4
+
+
+def mq(lib, shape, sliding=True, max_q=8, window=1024, ptrs=None):
+    p = ptrs or [FAKE] * 7
+    if sliding:
+        return lib.attn_multiquery_sliding(p[0], p[1], max_q, p[2], p[3], p[4], p[5], window, p[6],
+                                           ctypes.byref(shape), FAKE, 1 << 30, NULL)
+    return lib.attn_multiquery_global(p[0], p[1], max_q, p[2], p[4], p[5], p[6], ctypes.byref(shape),
+                                      FAKE, 1 << 30, NULL)
+
+
+def test_multiquery_validation(lib):
+    assert mq(lib, _shape(), max_q=0) == -1
+    assert mq(lib, _shape(), window=-1) == -1
+    assert mq(lib, _shape(), ptrs=[FAKE, NULL] + [FAKE] * 5) == -1
+    assert mq(lib, _shape(kv_dtype=B.DA_DTYPE_F32)) == -2
+    assert mq(lib, _shape(head_dim=512)) == -2
+    assert mq(lib, _shape(), max_q=(1 << 18) + 1) == -2
+    assert mq(lib, _gshape(), sliding=False, ptrs=[FAKE] * 6 + [NULL]) == -1
+    assert mq(lib, _gshape(group=8), sliding=False) == -2
+    n = ctypes.c_size_t(0)
+    assert lib.attn_multiquery_workspace_bytes(ctypes.byref(_shape()), 0, 1024, ctypes.byref(n)) == -1
+    assert lib.attn_multiquery_workspace_bytes(ctypes.byref(_shape()), 8, 1024, None) == -1
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_multiquery_no_device_reported_after_valid_arguments(lib):
+    assert mq(lib, _shape()) == -4
+    assert mq(lib, _gshape(), sliding=False) == -4
+    n = ctypes.c_size_t(0)
+    assert lib.attn_multiquery_workspace_bytes(ctypes.byref(_gshape()), 8, 0, ctypes.byref(n)) == -4
