@@ -79,6 +79,33 @@ def append_bytes(aw):
     return (B * Hq + kv_rows) * aw.D * (4 + esize) + 2 * aw.D * 4 + 2 * B * 4
 
 
+def multiquery_work(mq):
+    """Algorithmic bytes (keys some query sees, read once, K = V once on
+    global layers; q, fp32 out and block-table entries) and FLOPs (4 * D per
+    visible (query, head, key)) of one multi-query call."""
+    import numpy as np
+    base = mq.base
+    esize = 2
+    sliding = mq.kind == "sliding"
+    kv_bytes, flops, table = 0, 0, 0
+    for b in range(len(base.seq_lens)):
+        L, S = int(base.seq_lens[b]), int(mq.q_start[b + 1] - mq.q_start[b])
+        if S <= 0 or L <= 0:
+            continue
+        pos = L - S + np.arange(S, dtype=np.int64)
+        pos = pos[pos >= 0]
+        if len(pos) == 0:
+            continue
+        lo = max(0, int(pos.min()) - base.window + 1) if sliding else 0
+        n_keys = L - lo
+        kv_bytes += n_keys * base.Hkv * base.D * esize * (2 if sliding else 1)
+        table += ((L - 1) // 16 - lo // 16 + 1) * 4
+        vis = np.minimum(pos + 1, base.window) if sliding else pos + 1
+        flops += int(vis.sum()) * base.Hkv * base.G * base.D * 4
+    T, Hq, D = mq.q.shape
+    return kv_bytes + T * Hq * D * (esize + 4) + table, flops
+
+
 def time_calls(fn, n):
     """Mean µs per call of fn over n back-to-back calls (HIP events on the
     current stream, after one untimed call)."""
@@ -161,6 +188,7 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
     """The decode-step appends and the gated variants, timed after the step
     (not part of it): one new token per sequence at position L, the gate on
     the same outputs."""
+    import numpy as np
     import torch
     log("timing the decode-step appends and the gated calls")
     shp = dict(Hkv=sl.Hkv, G=sl.G, D=sl.D)
@@ -179,8 +207,37 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
     gsl_us = time_calls(lambda: da.attn_decode_sliding_gated(*d_sl[:5], sl.window, gate_sl, out=out_sl), n_extra)
     ggl_us = time_calls(lambda: da.attn_decode_global_gated(*d_gl, gate_gl, out=out_gl,
                                                             num_splits=num_splits), n_extra)
+    # several queries per sequence: 8 draft tokens per sequence (speculative
+    # verification) at the decode workloads' lengths, and one 2048-token
+    # prefill chunk per sequence of B = 4
+    mq_sl = I.make_multiquery("sliding", sl.seq_lens, np.full(64, 8), tag=(704,), P_max=2048, **shp,
+                              window=sl.window)
+    q8 = I.rms_rows(I.rng_for((705,), 0, I.STREAM_MQ), (64 * 8, gl.Hkv * gl.G, gl.D))
+    mq_gl = I.MultiQueryWorkload("global", I.to_storage(q8, "bf16"), np.arange(0, 65 * 8, 8, dtype=np.int32), gl)
+    pf_sl = I.make_multiquery("sliding", [4096] * 4, [2048] * 4, tag=(706,), **shp, window=sl.window)
+    pf_gl = I.make_multiquery("global", [8192] * 4, [2048] * 4, tag=(707,), **I.GLOBAL)
+    mq_res = {}
+    for name, mq in (("verify_sliding", mq_sl), ("verify_global", mq_gl), ("prefill_sliding", pf_sl),
+                     ("prefill_global", pf_gl)):
+        base = mq.base
+        args = [to_dev(mq.q), to_dev(mq.q_start), mq.max_queries]
+        tail = [to_dev(base.block_table), to_dev(base.seq_lens)]
+        o = torch.empty(mq.q.shape, dtype=torch.float32, device="cuda")
+        if mq.kind == "sliding":
+            caches = [to_dev(base.k_cache), to_dev(base.v_cache)] if base is not sl else d_sl[1:3]
+            fn = lambda: da.attn_multiquery_sliding(*args, *caches, *tail, base.window, out=o)
+        else:
+            caches = [d_gl[1]] if base is gl else [to_dev(base.kv_cache)]
+            fn = lambda: da.attn_multiquery_global(*args, *caches, *tail, out=o)
+        us = time_calls(fn, n_extra)
+        nbytes, flops = multiquery_work(mq)
+        mq_res[f"mq_{name}_us_per_call"] = round(us, 2)
+        mq_res[f"mq_{name}_GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        mq_res[f"mq_{name}_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 2)
+        del caches, fn, o
+    log("multi-query: " + ", ".join(f"{k}={v}" for k, v in mq_res.items()))
     gate_b = 64 * 16 * 4
-    extra = {
+    extra = {**mq_res,
         "append_sliding_us_per_call": round(app_sl_us, 2),
         "append_sliding_GBps": round(append_bytes(aws) / (app_sl_us * 1e-6) / 1e9, 1),
         "append_global_us_per_call": round(app_gl_us, 2),
