@@ -147,6 +147,23 @@ def scatter_tiled(cache, bt_row, positions, rows):
     cache[pages, :, :, positions % PAGE, :] = rows.reshape(n, hkv, D // x, x)
 
 
+def scatter_prenorm(cache, bt_row, positions, rows):
+    """Pre-norm layout [P][Hkv][64][16][8] of 512-wide rows: the 32-coordinate
+    block B of a row goes to chunks 32 (B % 2) + 4 (B // 2) .. +4 (so the
+    two coordinates d and d + 256 of a rotation pair share a chunk slot in
+    the same half), token t to slot t % 16 of page bt[t // 16]."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(bt_row, dtype=np.int64)[positions // PAGE]
+    n, hkv, D = rows.shape
+    assert D == 512
+    blocks = rows.reshape(n, hkv, 16, 4, 8)            # [.., block, chunk in block, 8]
+    phys = np.empty((n, hkv, 64, 8), dtype=rows.dtype)
+    for B in range(16):
+        c0 = 32 * (B % 2) + 4 * (B // 2)
+        phys[:, :, c0:c0 + 4, :] = blocks[:, :, B]
+    cache[pages, :, :, positions % PAGE, :] = phys
+
+
 # ----------------------------------------------------------------------------
 # block tables
 # ----------------------------------------------------------------------------
@@ -289,6 +306,53 @@ def make_global(seq_lens, *, Hkv=1, G=16, D=512, kv_dtype="bf16", tag=(200,),
     _parallel(fill_seq, range(B))
     return GlobalWorkload(to_storage(q, kv_dtype), kv, bt, seq_lens, kv_dtype, Hkv, G, D,
                           meta=dict(num_pages=num_pages, P_max=int(bt.shape[1])))
+
+
+@dataclass
+class PrenormWorkload:
+    q: np.ndarray            # [B, 16, 512] stored (normed and rotated query)
+    x_cache: np.ndarray      # pre-norm layout [P, 1, 64, 16, 8] stored
+    w_k: np.ndarray          # float32 [512]
+    block_table: np.ndarray
+    seq_lens: np.ndarray
+    kv_dtype: str
+    Hkv: int = 1
+    G: int = 16
+    D: int = 512
+
+
+def make_global_prenorm(seq_lens, *, kv_dtype="bf16", tag=(950,), layer=0, P_max=None, poison=True,
+                        chunk_tokens=8192):
+    """Global-layer cache holding the pre-norm kv projection of every token
+    (rows N(0, s^2), s log-uniform in [0.1, 10], as raw_rows draws them), the
+    k-norm weight, and queries as make_global draws them."""
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B, Hkv, G, D = len(seq_lens), 1, 16, 512
+    if P_max is None:
+        P_max = max(1, max((pages_for(L) for L in seq_lens), default=1))
+    ranges = [(0, pages_for(L)) if L > 0 else (0, 0) for L in seq_lens]
+    bt, num_pages = build_block_table(ranges, P_max, rng_for(tag, layer, STREAM_PERM))
+    dt = storage_np_dtype(kv_dtype)
+    fill = storage_nan(kv_dtype) if poison else dt(0)
+    xc = np.empty((num_pages, Hkv, 64, PAGE, 8), dtype=dt)
+    xc[num_pages - 1] = fill
+    w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D)
+    w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D).astype(np.float32)
+    q = rms_rows(rng_for(tag, layer, STREAM_Q), (B, Hkv * G, D), w_q)
+
+    def fill_seq(b):
+        L = int(seq_lens[b])
+        if L <= 0:
+            return
+        if L % PAGE:
+            xc[bt[b, pages_for(L) - 1], :, :, L % PAGE:, :] = fill
+        rk = rng_for(tag, layer, [STREAM_RAW_K, b])
+        for t0 in range(0, L, chunk_tokens):
+            pos = np.arange(t0, min(L, t0 + chunk_tokens))
+            scatter_prenorm(xc, bt[b], pos, to_storage(raw_rows(rk, (len(pos), Hkv, D)), kv_dtype))
+
+    _parallel(fill_seq, range(B))
+    return PrenormWorkload(to_storage(q, kv_dtype), xc, w_k, bt, seq_lens, kv_dtype)
 
 
 # ----------------------------------------------------------------------------

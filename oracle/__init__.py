@@ -47,6 +47,9 @@ from .paged import (  # noqa: F401
     multiquery_positions,
     paged_multiquery_sliding,
     paged_multiquery_global,
+    prenorm_chunk_of,
+    gather_prenorm_cache,
+    paged_decode_global_prenorm,
     f64_to_bf16_bits,
 )
 from .norm_rope import (  # noqa: F401

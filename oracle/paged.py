@@ -21,6 +21,7 @@ Stored values are decoded exactly to float64 (bf16 bit patterns are the top
 import numpy as np
 
 from .attention import causal_gqa, decode_gqa, sliding_decode_gqa, sliding_gqa
+from .norm_rope import rmsnorm, rmsnorm_unit, rope
 
 PAGE = 16  # tokens per page (Model Spec page, "At a glance", shape domain)
 
@@ -58,6 +59,59 @@ def gather_tiled_cache(cache, bt_row, positions):
     sub = cache[pages, :, :, slots, :]          # [n, Hkv, D/x, x]
     n, hkv, nx, x = sub.shape
     return sub.reshape(n, hkv, nx * x)
+
+
+def prenorm_chunk_of(d):
+    """Chunk (of 64 per token) holding coordinate d of a 512-wide pre-norm
+    row in the pre-norm cache layout: the 32-coordinate block B = d // 32
+    goes to half B % 2, slot B // 2 of that half, and its 4 chunks of 8 in
+    order, i.e. chunk 32 * (B % 2) + 4 * (B // 2) + (d % 32) // 8."""
+    d = np.asarray(d)
+    B = d // 32
+    return 32 * (B % 2) + 4 * (B // 2) + (d % 32) // 8
+
+
+def gather_prenorm_cache(cache, bt_row, positions):
+    """Rows x[t, :, :] ([n, Hkv, 512], stored dtype) of a pre-norm paged
+    cache ``[num_pages][Hkv][64][16][8]``: coordinate d of token t, KV head c
+    is ``cache[bt[t // 16], c, prenorm_chunk_of(d), t % 16, d % 8]``."""
+    positions = np.asarray(positions, dtype=np.int64)
+    pages = np.asarray(bt_row, dtype=np.int64)[positions // PAGE]
+    sub = cache[pages, :, :, positions % PAGE, :]   # [n, Hkv, 64 chunks, 8]
+    d = np.arange(512)
+    return sub[:, :, prenorm_chunk_of(d), d % 8]
+
+
+PRENORM_EPS = 1e-6
+PRENORM_ROPE = dict(theta=1000000.0, rot=512, denom=512, active=64)
+
+
+def paged_decode_global_prenorm(q, x_cache, w_k, block_table, seq_lens, kv_dtype, scale=1.0):
+    """Global decode from the shared pre-norm projection x (Model Spec page,
+    "Compute-graph nodes": on global layers one 512-wide projection feeds
+    ``attn.qk_norm`` with ``attn.rope`` as k, and ``attn.v_norm`` as v):
+    k[l] = rope(pos l, rmsnorm(eps, x[l], w_k)) with theta 10^6, rot = denom
+    = 512, active 64; v[l] = rmsnormUnit(eps, x[l]); then decodeGQA.
+
+    q : [B, Hkv*G, 512] stored (already normed and rotated); x_cache : the
+    pre-norm layout; w_k : [512]; returns float64 [B, Hkv*G, 512].
+    """
+    qf = stored_to_f64(q, kv_dtype)
+    B, Hq, D = qf.shape
+    Hkv = x_cache.shape[1]
+    G = Hq // Hkv
+    w = np.asarray(w_k, dtype=np.float64)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        pos = np.arange(L)
+        x = stored_to_f64(gather_prenorm_cache(x_cache, block_table[b], pos), kv_dtype)  # [L, Hkv, D]
+        k = rope(pos=pos[:, None], x=rmsnorm(PRENORM_EPS, x, w), **PRENORM_ROPE)
+        v = rmsnorm_unit(PRENORM_EPS, x)
+        out[b] = decode_gqa(scale, qf[b].reshape(Hkv, G, D), k, v).reshape(Hq, D)
+    return out
 
 
 def sliding_visible_range(L, window):
