@@ -236,6 +236,15 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
         mq_res[f"mq_{name}_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 2)
         del caches, fn, o
     log("multi-query: " + ", ".join(f"{k}={v}" for k, v in mq_res.items()))
+    # global decode from the pre-norm projection at the global workload's lengths
+    pw = I.make_global_prenorm(gl.seq_lens, tag=(708,), P_max=2048)
+    d_pw = [to_dev(x) for x in (pw.q, pw.x_cache, pw.w_k, pw.block_table, pw.seq_lens)]
+    o_pw = torch.empty((64, 16, 512), dtype=torch.float32, device="cuda")
+    pre_us = time_calls(lambda: da.attn_decode_global_prenorm(*d_pw, out=o_pw, num_splits=num_splits), n_extra)
+    mq_res["global_prenorm_us_per_call"] = round(pre_us, 2)
+    mq_res["global_prenorm_GBps"] = round((sum(gb.values()) + 512 * 4) / (pre_us * 1e-6) / 1e9, 1)
+    log(f"global prenorm {pre_us:.1f} us")
+    del d_pw, o_pw
     gate_b = 64 * 16 * 4
     extra = {**mq_res,
         "append_sliding_us_per_call": round(app_sl_us, 2),

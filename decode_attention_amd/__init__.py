@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     attn_decode_global_workspace_bytes,
     attn_decode_sliding_gated,
     attn_decode_global_gated,
+    attn_decode_global_prenorm,
     attn_kv_append_sliding,
     attn_kv_append_global,
     attn_multiquery_sliding,

@@ -44,7 +44,7 @@ class DaShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
-           "attn_decode_sliding_gated", "attn_decode_global_gated",
+           "attn_decode_sliding_gated", "attn_decode_global_gated", "attn_decode_global_prenorm",
            "attn_kv_append_sliding", "attn_kv_append_global",
            "attn_multiquery_sliding", "attn_multiquery_global", "attn_multiquery_workspace_bytes",
            "attn_status_string")
@@ -78,6 +78,9 @@ def load_library():
         lib.attn_decode_global_gated.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
                                                  ctypes.c_size_t, vp]
         lib.attn_decode_global_gated.restype = ctypes.c_int32
+        lib.attn_decode_global_prenorm.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
+                                                   ctypes.c_size_t, vp]
+        lib.attn_decode_global_prenorm.restype = ctypes.c_int32
         lib.attn_decode_global_workspace_bytes.argtypes = [ctypes.POINTER(DaShape),
                                                            ctypes.POINTER(ctypes.c_size_t)]
         lib.attn_decode_global_workspace_bytes.restype = ctypes.c_int32
@@ -233,7 +236,18 @@ def attn_decode_global_gated(q, kv_cache, block_table, seq_lens, gate, out=None,
     return _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits, stream)
 
 
-def _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits, stream):
+def attn_decode_global_prenorm(q, x_cache, w_k, block_table, seq_lens, out=None, workspace=None, num_splits=0,
+                               stream=None):
+    """decodeGQA over the pre-norm cache: k = rope(rmsnorm(x, w_k)), v =
+    rmsnormUnit(x) derived in the kernel. q bf16 [B, 16, 512]; x_cache bf16
+    [P, 1, 64, 16, 8] (pre-norm layout); w_k fp32 [512]."""
+    import torch
+    _require(w_k.dtype == torch.float32 and w_k.is_contiguous() and w_k.device == q.device
+             and tuple(w_k.shape) == (512,), "w_k must be contiguous fp32 [512] on q's device")
+    return _global(q, x_cache, block_table, seq_lens, None, out, workspace, num_splits, stream, w_k=w_k)
+
+
+def _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits, stream, w_k=None):
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (kv_cache,))
@@ -253,7 +267,10 @@ def _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits
             _workspaces[key] = workspace
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if gate is None:
+    if w_k is not None:
+        _check(lib.attn_decode_global_prenorm(_ptr(q), _ptr(kv_cache), _ptr(w_k), _ptr(block_table),
+                                              _ptr(seq_lens), _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st))
+    elif gate is None:
         _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
                                       ctypes.byref(shape), ws_ptr, ws_bytes, st))
     else:

@@ -22,6 +22,12 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Wall", "-Wno-unused-function"]
 
 
+# Per-file flags. The global kernel's 6-step descriptor loop must unroll fully
+# (its ring and descriptors live in registers only then); the pre-norm
+# variant's body exceeds LLVM's default size limit for a requested unroll.
+FILE_FLAGS = {"global.hip": ["-mllvm", "-pragma-unroll-threshold=60000"]}
+
+
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -32,7 +38,7 @@ def hipcc():
 def _compile(src, verbose, extra):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [hipcc(), *HIP_FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (res.stderr or "").splitlines() if "not a recognized feature" not in l]
     if res.returncode != 0:

@@ -86,7 +86,7 @@ da_status decode_sliding(const void* q, const void* k_cache, const void* v_cache
 
 da_status decode_global(const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
                         const float* gate, void* out, const da_shape* shape, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, const float* w_k = nullptr) {
   da_status st = check_global_shape(shape);
   if (st != DA_OK) return st;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
@@ -96,7 +96,7 @@ da_status decode_global(const void* q, const void* kv_cache, const int32_t* bloc
   const int splits = da::global_num_splits(*shape, cus);
   const size_t need = da::global_workspace_bytes(*shape, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
-  return da::launch_global(q, kv_cache, block_table, seq_lens, gate, out, *shape, splits, workspace,
+  return da::launch_global(q, kv_cache, block_table, seq_lens, gate, w_k, out, *shape, splits, workspace,
                            (hipStream_t)stream);
 }
 
@@ -199,6 +199,14 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                              void* workspace, size_t workspace_bytes, void* stream) {
   return decode_global(q, kv_cache, block_table, seq_lens, nullptr, out, shape, workspace, workspace_bytes,
                        stream);
+}
+
+da_status attn_decode_global_prenorm(const void* q, const void* x_cache, const float* w_k,
+                                     const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                     const da_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w_k) return DA_ERR_INVALID_ARG;
+  return decode_global(q, x_cache, block_table, seq_lens, nullptr, out, shape, workspace, workspace_bytes, stream,
+                       w_k);
 }
 
 da_status attn_decode_global_gated(const void* q, const void* kv_cache, const int32_t* block_table,

@@ -40,6 +40,21 @@
 // Loads run ahead of the compute across segment and sequence boundaries:
 // page ids 4 steps, page slices 2 steps; a segment change costs a q reload
 // and an LDS merge, not a pipeline restart.
+//
+// Pre-norm variant (PRE): the cache holds the shared pre-norm projection x
+// of every token (Model Spec compute-graph nodes attn.qk_norm, attn.v_norm,
+// attn.rope on global layers: k = rope(rmsnorm(x, w_k)), v = rmsnormUnit(x);
+// Op Specs Norm.lean and Rope.lean, theta 1e6, rot = denom = 512, the first
+// 64 frequencies active). With r = 1/sqrt(mean(x^2) + eps) per token,
+//   q . k = r * (q . R(x * w_k))   and   v = r * x,
+// so the page is still read once: r scales the score and the weight p of
+// the PV product (the denominator keeps p), w_k moves onto q for the 384
+// coordinates RoPE leaves alone (q * w_k as bf16 hi + lo, two MFMAs), and the
+// 128 rotated coordinates are rotated in fp32 in registers and enter the
+// MFMA as bf16 hi + lo. The cache layout puts the 32-coordinate block B in
+// half B % 2, k-step B / 2, so a rotation pair (d, d + 256), d < 64, sits in
+// one lane: k-steps 0 and 4 of each half. Angles: pos * theta^(-d/256) in
+// revolutions, in fp64, wrapped to [-1/2, 1/2] before the fp32 sin/cos.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -74,6 +89,7 @@ constexpr size_t kGHeaderBytes = 16384;  // >= (2*kGMaxBatch + 1) ints
 static_assert((2 * kGMaxBatch + 1) * sizeof(int) <= kGHeaderBytes, "header too small");
 
 struct GlobalArgs {
+  const float* w_k;          // pre-norm variant: k-norm weight [512]; else null
   const uint16_t* q;         // [B][16][512] bf16 bits
   const uint16_t* kv;        // [P][1][64][16][8] bf16 bits
   const int32_t* bt;         // [B][P_max]
@@ -140,6 +156,32 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+constexpr double kPreTheta = 1000000.0;  // RoPE base of the global layers
+constexpr int kPreActive = 64;           // active frequencies (pairs d, d + 256 with d < 64)
+constexpr float kPreEps = 1e-6f;
+
+// Dword e (compile-time after unrolling) of a uint4 held in registers;
+// taking the address of a register array would move it to scratch.
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int e) {
+  return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ uint32_t pack_bf16(__bf16 lo, __bf16 hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+}
+
+// Logical coordinate of element e of k-step i of half hf, lane group g, in
+// the pre-norm layout (block 2i + hf), or in the K=V layout.
+template <bool PRE>
+__device__ __forceinline__ int coord_of(int hf, int i, int g) {
+  return PRE ? 64 * i + 32 * hf + 8 * g : kGSlice * hf + 32 * i + 8 * g;
+}
+// First coordinate of output tile t (16 coordinates) of half hf.
+template <bool PRE>
+__device__ __forceinline__ int tile_coord(int hf, int t) {
+  return PRE ? 64 * (t >> 1) + 32 * hf + 16 * (t & 1) : kGSlice * hf + 16 * t;
+}
+
+template <bool PRE>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) void global_decode_kernel(GlobalArgs a) {
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
@@ -150,7 +192,21 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   __shared__ float s_ml[4][2][kWave];           // m, l of the wave states being merged
   // Q^T B operands of the current segment: [half][k-step][lane], lane h + 16g
   // holding head h, coordinates 256*half + 32*kstep + 8g .. +8
-  __shared__ uint4 s_q[kGPair][kGKSteps][kWave];
+  // (PRE: [half][k-step][hi, lo][lane]: q * w_k split into bf16 hi and lo on
+  // unrotated k-steps, q twice on the rotated ones)
+  constexpr int kQParts = PRE ? 2 : 1;
+  __shared__ uint4 s_q[kGPair][kGKSteps][kQParts][kWave];
+  __shared__ double s_g[PRE ? kPreActive : 1];      // theta^(-d/256) / (2 pi): revolutions per position
+  __shared__ float2 s_w[PRE ? kPreActive : 1];      // (w_k[d], w_k[d + 256])
+  __shared__ float s_ss[PRE ? 2 : 1][kGWaves][16];  // per-token sums of squares of each wave's half
+
+  if constexpr (PRE) {
+    const int i = threadIdx.x;
+    if (i < kPreActive) {
+      s_g[i] = pow(kPreTheta, -(double)i / 256.0) * 0.15915494309189535;  // 1 / (2 pi)
+      s_w[i] = make_float2(a.w_k[i], a.w_k[i + 256]);
+    }
+  }
 
   build_prefix(a, s_pre, s_len, s_tmp);
   const int N = rfl(s_pre[a.B]);
@@ -201,13 +257,38 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     uint4 t[2];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int u = 2 * tid + r;  // s_q element: half, k-step, lane
+      const int u = 2 * tid + r;  // half, k-step, lane
       const int f = u / (kGKSteps * kWave), i = (u / kWave) % kGKSteps, l = u % kWave;
-      t[r] = ld16(a.q + ((size_t)b * kGH + (l & 15)) * kGD + f * kGSlice + 32 * i + 8 * (l >> 4));
+      t[r] = ld16(a.q + ((size_t)b * kGH + (l & 15)) * kGD + coord_of<PRE>(f, i, l >> 4));
     }
     wait_vmem_all();
+    if constexpr (!PRE) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) (&s_q[0][0][0])[2 * tid + r] = t[r];
+      for (int r = 0; r < 2; ++r) (&s_q[0][0][0][0])[2 * tid + r] = t[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int u = 2 * tid + r;
+        const int f = u / (kGKSteps * kWave), i = (u / kWave) % kGKSteps, l = u % kWave;
+        uint4 hi = t[r], lo = t[r];
+        if (i % 4 != 0) {  // unrotated: q * w_k as hi + lo
+          const int d0 = coord_of<true>(f, i, l >> 4);
+          uint32_t ph[4], pl[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t qw = u4_get(t[r], e);
+            const float v0 = bf16_lo(qw) * a.w_k[d0 + 2 * e], v1 = bf16_hi(qw) * a.w_k[d0 + 2 * e + 1];
+            const __bf16 h0 = (__bf16)v0, h1 = (__bf16)v1;
+            ph[e] = pack_bf16(h0, h1);
+            pl[e] = pack_bf16((__bf16)(v0 - (float)h0), (__bf16)(v1 - (float)h1));
+          }
+          hi = make_uint4(ph[0], ph[1], ph[2], ph[3]);
+          lo = make_uint4(pl[0], pl[1], pl[2], pl[3]);
+        }
+        s_q[f][i][0][l] = hi;
+        s_q[f][i][1][l] = lo;
+      }
+    }
     __syncthreads();
   };
 
@@ -249,17 +330,18 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       lt += xor32(lt);
       const int pb = rfl(s_pre[seg_b]), pe = rfl(s_pre[seg_b + 1]);
       if (seg_first == pb && seg_end == pe) {  // whole sequence: o[b][h][d]
-        float* dst = a.out + ((size_t)seg_b * kGH + lh) * kGD + hf * kGSlice + 4 * lg;
+        float* dst = a.out + ((size_t)seg_b * kGH + lh) * kGD + 4 * lg;
         const float inv = 1.f / lt;
 #pragma unroll
         for (int t = 0; t < kGMTiles; ++t) {
           f32x4 o = acc[t] * inv;
+          const int dt = tile_coord<PRE>(hf, t);
           if (a.gate) {  // sigmoidGate epilogue (set only when no merge follows)
-            const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (dst - a.out) + t * 16);
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (dst - a.out) + dt);
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
           }
-          *reinterpret_cast<f32x4*>(dst + t * 16) = o;
+          *reinterpret_cast<f32x4*>(dst + dt) = o;
         }
       } else {  // partial slot, lane order: 1 KB contiguous per store
         const int slot = 2 * w + (seg_first == R0 ? 0 : 1);
@@ -330,18 +412,86 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       const int P = dP[d], n = dN[d], b = dB[d];
       const int L = dL[d];
       const int j = dJ[d] + pr;  // this pair's page within sequence b
-      // all LDS reads first, then the MFMAs (the scheduler would otherwise
-      // pay the LDS latency once per MFMA)
-      uint4 qv[kGKSteps];
-#pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) qv[i] = s_q[hf][i][lane];
-      __builtin_amdgcn_sched_barrier(0);
       f32x4 s2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if constexpr (!PRE) {
+        // all LDS reads first, then the MFMAs (the scheduler would otherwise
+        // pay the LDS latency once per MFMA)
+        uint4 qv[kGKSteps];
 #pragma unroll
-      for (int i = 0; i < kGKSteps; ++i)
-        s2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[bs][i]),
-                                                            __builtin_bit_cast(bf16x8, qv[i]), s2[i & 1],
-                                                            0, 0, 0);
+        for (int i = 0; i < kGKSteps; ++i) qv[i] = s_q[hf][i][0][lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kGKSteps; ++i)
+          s2[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[bs][i]),
+                                                              __builtin_bit_cast(bf16x8, qv[i]), s2[i & 1],
+                                                              0, 0, 0);
+      } else {
+        // sum of squares of this wave's 256 coordinates of token lane & 15
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < kGKSteps; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = dot2_bf16(u4_get(buf[bs][i], e), u4_get(buf[bs][i], e), ss);
+        ss += xor16(ss);
+        ss += xor32(ss);
+        if (g == 0) s_ss[xb][wv][lane] = ss;
+        // RoPE of the pairs (d, d + 256), d = 32 hf + 8 g + e: elements e of
+        // k-steps 0 and 4, at position 16 j + (lane & 15); rotated k as hi + lo
+        uint4 kr[2][2];  // [k-step 0 / 4][hi / lo]
+        {
+          const double posd = (double)(j * kPage + (lane & 15));
+          uint32_t k0h[4], k0l[4], k4h[4], k4l[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            __bf16 vh0[2], vl0[2], vh4[2], vl4[2];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+              const int dd = 32 * hf + 8 * g + 2 * e2 + hb;
+              double rev = posd * s_g[dd];
+              rev -= rint(rev);  // wrapped to [-1/2, 1/2] revolutions
+              float sn, cs;
+              __sincosf((float)rev * 6.28318530717958648f, &sn, &cs);
+              const float2 w2 = s_w[dd];
+              const uint32_t u0 = u4_get(buf[bs][0], e2), u4 = u4_get(buf[bs][4], e2);
+              const float xa = w2.x * (hb ? bf16_hi(u0) : bf16_lo(u0));
+              const float xb = w2.y * (hb ? bf16_hi(u4) : bf16_lo(u4));
+              const float k0 = cs * xa - sn * xb, k4 = cs * xb + sn * xa;
+              vh0[hb] = (__bf16)k0;
+              vl0[hb] = (__bf16)(k0 - (float)vh0[hb]);
+              vh4[hb] = (__bf16)k4;
+              vl4[hb] = (__bf16)(k4 - (float)vh4[hb]);
+            }
+            k0h[e2] = pack_bf16(vh0[0], vh0[1]);
+            k0l[e2] = pack_bf16(vl0[0], vl0[1]);
+            k4h[e2] = pack_bf16(vh4[0], vh4[1]);
+            k4l[e2] = pack_bf16(vl4[0], vl4[1]);
+          }
+          kr[0][0] = make_uint4(k0h[0], k0h[1], k0h[2], k0h[3]);
+          kr[0][1] = make_uint4(k0l[0], k0l[1], k0l[2], k0l[3]);
+          kr[1][0] = make_uint4(k4h[0], k4h[1], k4h[2], k4h[3]);
+          kr[1][1] = make_uint4(k4l[0], k4l[1], k4l[2], k4l[3]);
+        }
+        // k-steps 0, 4: (k hi, q) + (k lo, q); others: (x, q w hi) + (x, q w lo)
+#pragma unroll
+        for (int i0 = 0; i0 < kGKSteps; i0 += 4) {
+          uint4 qh[4], ql[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            qh[u] = s_q[hf][i0 + u][0][lane];
+            ql[u] = s_q[hf][i0 + u][1][lane];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint4 a1 = u == 0 ? kr[i0 / 4][0] : buf[bs][i0 + u];
+            const uint4 a2 = u == 0 ? kr[i0 / 4][1] : buf[bs][i0 + u];
+            s2[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                            __builtin_bit_cast(bf16x8, qh[u]), s2[0], 0, 0, 0);
+            s2[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a2),
+                                                            __builtin_bit_cast(bf16x8, ql[u]), s2[1], 0, 0, 0);
+          }
+        }
+      }
       s_part[xb][wv][lane] = s2[0] + s2[1];
 #pragma unroll
       for (int i = 0; i < kGKSteps; ++i) *reinterpret_cast<uint4*>(vs + i * 512 + lane * 8) = buf[bs][i];
@@ -354,6 +504,14 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       }
       __syncthreads();
       const f32x4 s = s_part[xb][wv & ~1][lane] + s_part[xb][wv | 1][lane];
+      float rr[4] = {1.f, 1.f, 1.f, 1.f};  // PRE: 1 / rms of tokens 4g .. 4g+3
+      if constexpr (PRE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sst = s_ss[xb][wv & ~1][4 * g + e] + s_ss[xb][wv | 1][4 * g + e];
+          rr[e] = 1.f / sqrtf(sst * (1.f / kGD) + kPreEps);
+        }
+      }
       xb ^= 1;
       if (n == 0) return false;  // past the end: the open segment is flushed after the loop
       if (!seg_active) {
@@ -365,7 +523,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       if (pr < n) {
         float sc[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sc[e] = s[e] * kLog2e;
+        for (int e = 0; e < 4; ++e) sc[e] = (PRE ? s[e] * rr[e] : s[e]) * kLog2e;
         if (edge) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -392,12 +550,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
         // P^T operand: k-slots 8g..8g+3 hold bf16(p) of tokens 4g..4g+3 and
         // 8g+4..8g+7 the remainder bf16(p - bf16(p)); the V^T operand
         // repeats the same 4 tokens in both halves.
+        // (PRE: the PV weight is p * r, since v = r * x; a masked token's r
+        // may be NaN, so its weight is set, not multiplied)
         bf16x8 pp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float pv = exp2_fast(sc[e] - m_run);
-          pp[e] = (__bf16)pv;
-          pp[4 + e] = (__bf16)(pv - (float)pp[e]);
+          const float pw = PRE ? (sc[e] == -INFINITY ? 0.f : pv * rr[e]) : pv;
+          pp[e] = (__bf16)pw;
+          pp[4 + e] = (__bf16)(pw - (float)pp[e]);
           l_run += pv;
         }
         constexpr int kVB = DA_GLOBAL_VT_BATCH;  // transposed reads in flight per batch
@@ -469,7 +630,8 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int grp = threadIdx.x / kWave;
   const int h = lane & 15, g = lane >> 4;
-  const int d0 = (T / kGMTiles) * kGSlice + (T % kGMTiles) * 16 + 4 * g;
+  const int Tt = T % kGMTiles, Th = T / kGMTiles;  // tile, half
+  const int d0 = (a.w_k ? 64 * (Tt >> 1) + 32 * Th + 16 * (Tt & 1) : kGSlice * Th + 16 * Tt) + 4 * g;
   float* ob = a.out + ((size_t)b * kGH + h) * kGD + d0;
   // sigmoidGate epilogue operands, loaded first so that their latency hides
   // behind the header reads: the gate, and the row as the decode kernel wrote
@@ -575,9 +737,10 @@ size_t global_workspace_bytes(const da_shape& s, int num_splits) {
 }
 
 da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
-                        const int32_t* seq_lens, const float* gate, void* out, const da_shape& s,
-                        int num_splits, void* workspace, hipStream_t stream) {
+                        const int32_t* seq_lens, const float* gate, const float* w_k, void* out,
+                        const da_shape& s, int num_splits, void* workspace, hipStream_t stream) {
   GlobalArgs a;
+  a.w_k = w_k;
   a.q = (const uint16_t*)q;
   a.kv = (const uint16_t*)kv_cache;
   a.bt = block_table;
@@ -592,7 +755,10 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   a.B = s.batch;
   a.P_max = s.max_pages_per_seq;
   a.G = num_splits;
-  hipLaunchKernelGGL(global_decode_kernel, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
+  if (w_k)
+    hipLaunchKernelGGL(global_decode_kernel<true>, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(global_decode_kernel<false>, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   if (num_splits <= 1) return DA_OK;  // nothing was split: no merge
   a.gate = gate;

@@ -144,6 +144,31 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Global decode from the shared pre-norm projection (pages: gemma-4-12b Model
+ * Spec, compute-graph nodes attn.qk_norm, attn.v_norm, attn.rope of the
+ * global layers; Op Specs Norm.lean rmsnorm / rmsnormUnit and Rope.lean rope).
+ * The cache holds, per token, the 512-wide kv projection x before its norms;
+ * the call derives, for every cached position l,
+ *   k[l] = rope(pos l, rmsnorm(1e-6, x[l], w_k))   (theta 1e6, rot = denom =
+ *          512, the first 64 frequencies active: pairs (d, d + 256), d < 64)
+ *   v[l] = rmsnormUnit(1e-6, x[l])
+ * and computes decodeGQA(q, k, v) as attn_decode_global does, reading each
+ * page once. q is the already normed and rotated query.
+ *
+ *   x_cache : bf16 [num_pages][1][64][16][8]: coordinate d of token t is
+ *             element [block_table[b][t/16]][0][32*(B%2) + 4*(B/2) + (d%32)/8]
+ *             [t%16][d%8] with B = d/32 (each 32-coordinate block B in half
+ *             B%2, so the pair (d, d + 256) shares a chunk slot of one half).
+ *   w_k     : fp32 [512] device array, the k-norm weight.
+ *   Everything else (shape limits, workspace, out, NaN in unread storage)
+ *   as for attn_decode_global; the workspace size is the same.
+ */
+da_status attn_decode_global_prenorm(const void* q, const void* x_cache, const float* w_k,
+                                     const int32_t* block_table, const int32_t* seq_lens, void* out,
+                                     const da_shape* shape, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
  * attn_decode_sliding and attn_decode_global followed by the output gate of
  * gated attention, o * sigmoid(gate) elementwise (pages: Op Specs of
  * google/gemma-4-12B, Attention.lean sigmoidGate; Op Specs overview, "Scalar

@@ -197,3 +197,14 @@ def test_multiquery_no_device_reported_after_valid_arguments(lib):
     assert mq(lib, _gshape(), sliding=False) == -4
     n = ctypes.c_size_t(0)
     assert lib.attn_multiquery_workspace_bytes(ctypes.byref(_gshape()), 8, 0, ctypes.byref(n)) == -4
+
+
+def test_prenorm_validation(lib):
+    def call(shape, ptrs=None, w=FAKE):
+        p = ptrs or [FAKE] * 5
+        return lib.attn_decode_global_prenorm(p[0], p[1], w, p[2], p[3], p[4], ctypes.byref(shape), FAKE, 1 << 30,
+                                              NULL)
+    assert call(_gshape(), w=NULL) == -1
+    assert call(_gshape(), ptrs=[FAKE, NULL, FAKE, FAKE, FAKE]) == -1
+    assert call(_gshape(group=8)) == -2
+    assert call(_gshape(kv_dtype=B.DA_DTYPE_F32)) == -2
