@@ -215,6 +215,10 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[i] = s_pre[i];
     for (int i = threadIdx.x; i < a.B; i += blockDim.x) a.ws_hdr[a.B + 1 + i] = s_len[i];
   }
+  if (w == 0 && a.ws_hdr == nullptr) {  // no merge follows: rows of empty sequences are 0 here
+    for (int i = threadIdx.x; i < a.B * (kGH * kGD / 4); i += blockDim.x)
+      if (s_len[i / (kGH * kGD / 4)] == 0) reinterpret_cast<f32x4*>(a.out)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = rfl(threadIdx.x / kWave);

@@ -10,7 +10,7 @@ import pytest
 import oracle
 from decode_attention_amd import inputs as I
 
-from gpu_util import BF16_TOL, global_on_gpu, max_abs
+from gpu_util import BF16_TOL, dev, global_on_gpu, max_abs
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,22 @@ def test_deterministic(gpu_lib):
     wl = I.make_global([10000, 3, 777], kv_dtype="bf16", tag=(404,), **I.GLOBAL)
     for splits in (0, 37, 256):
         assert np.array_equal(global_on_gpu(wl, splits), global_on_gpu(wl, splits))
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_empty_sequences_are_written(gpu_lib, num_splits):
+    # Rows of sequences without cached tokens are zero even where the output
+    # buffer held NaN, whatever the split.
+    import torch
+    import decode_attention_amd as da
+    wl = I.make_global([0, 40, 0, 3000, 0], kv_dtype="bf16", tag=(407,), **I.GLOBAL)
+    q, kv, bt, sl = (dev(x) for x in (wl.q, wl.kv_cache, wl.block_table, wl.seq_lens))
+    out = torch.full(tuple(q.shape), float("nan"), dtype=torch.float32, device="cuda")
+    da.attn_decode_global(q, kv, bt, sl, out=out, num_splits=num_splits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(got[[0, 2, 4]] == 0)
+    assert max_abs(got[[1, 3]], oracle_rows(wl, [1, 3])) <= BF16_TOL
 
 
 def test_config2_full_size_sampled(gpu_lib):
