@@ -262,6 +262,78 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
     return extra
 
 
+def time_sweep(da, I, n_steps):
+    """The full decode step of the model: 48 layer calls (layer i global iff
+    i % 6 == 5) at B = 256, lengths log-uniform in [1, 131072], every layer
+    with its own caches (drawn on the device). Timed after the B = 64 step,
+    not part of it."""
+    import types
+    import numpy as np
+    import torch
+    sl = I.sweep_seq_lens()
+    t = time.perf_counter()
+    layers = []
+    for i in range(I.SWEEP["layers"]):
+        layers.append(I.device_layer(I.sweep_kind(i), sl, layer=i))
+    torch.cuda.synchronize()
+    log(f"sweep: 48 layers drawn on the device in {time.perf_counter() - t:.1f} s "
+        f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB allocated)")
+    outs = {k: torch.empty((len(sl), 16, d), dtype=torch.float32, device="cuda")
+            for k, d in (("sliding", 256), ("global", 512))}
+
+    def call(dl):
+        if dl.kind == "sliding":
+            da.attn_decode_sliding(dl.q, *dl.caches, dl.block_table, dl.seq_lens, dl.window, out=outs["sliding"])
+        else:
+            da.attn_decode_global(dl.q, *dl.caches, dl.block_table, dl.seq_lens, out=outs["global"])
+
+    def wl(dl):
+        return types.SimpleNamespace(seq_lens=dl.host_seq_lens, window=dl.window, kv_dtype="bf16",
+                                     Hkv=dl.Hkv, G=dl.G, D=dl.D)
+
+    nbytes = {k: 0 for k in ("sliding", "global")}
+    for dl in layers:
+        f = sliding_bytes if dl.kind == "sliding" else global_bytes
+        nbytes[dl.kind] += sum(f(wl(dl)).values())
+    for dl in layers:  # warm-up step
+        call(dl)
+    torch.cuda.synchronize()
+    # per-call event times over one step
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+    for dl, (e0, e1) in zip(layers, ev):
+        e0.record()
+        call(dl)
+        e1.record()
+    torch.cuda.synchronize()
+    us = {k: [] for k in ("sliding", "global")}
+    for dl, (e0, e1) in zip(layers, ev):
+        us[dl.kind].append(e0.elapsed_time(e1) * 1e3)
+    # whole steps back to back
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        for dl in layers:
+            call(dl)
+    torch.cuda.synchronize()
+    step_ms = (time.perf_counter() - t0) / n_steps * 1e3
+    total = nbytes["sliding"] + nbytes["global"]
+    res = {
+        "sweep_workload": "48 layer calls (8 global D=512 K=V, 40 sliding D=256 w=1024), B=256, "
+                          "seq_lens log-uniform [1,131072], own caches per layer",
+        "sweep_ms_per_step": round(step_ms, 3),
+        "sweep_bytes_per_step": int(total),
+        "sweep_GBps": round(total / (step_ms * 1e-3) / 1e9, 1),
+        "sweep_frac_of_peak": round(total / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "sweep_sliding_us_per_call": round(float(np.mean(us["sliding"])), 2),
+        "sweep_global_us_per_call": round(float(np.mean(us["global"])), 2),
+        "sweep_sliding_GBps": round(nbytes["sliding"] / 40 / (np.mean(us["sliding"]) * 1e-6) / 1e9, 1),
+        "sweep_global_GBps": round(nbytes["global"] / 8 / (np.mean(us["global"]) * 1e-6) / 1e9, 1),
+    }
+    log("sweep: " + ", ".join(f"{k}={v}" for k, v in res.items() if k != "sweep_workload"))
+    del layers, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +344,8 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once, so that a "
                          "counter profile holds a plain copy of known size to scale HBM counters")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the 48-call full-step sweep at B = 256 (its caches take ~80 GB of HBM)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the append and gated-call timings after the step (so that a kernel "
                          "trace holds the step's dispatches only)")
@@ -350,6 +424,8 @@ def main():
 
     extra = {} if args.no_extras else time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb,
                                                   max(args.steps, 10), args.num_splits)
+    if not (args.no_extras or args.no_sweep):
+        extra.update(time_sweep(da, I, 5))
 
     current = counters_current() and args.num_splits == 0  # counters taken at the default split
     traffic = GLOBAL_TRAFFIC["bytes_per_call"] if current else None

@@ -517,3 +517,145 @@ def config_workload(cfg, layer=0):
         return make_global([131072, 262144], kv_dtype="bf16", tag=(3,), layer=layer,
                            P_max=16384, **GLOBAL)
     raise ValueError(cfg)
+
+
+# ----------------------------------------------------------------------------
+# the 48-call decode-step sweep, generated on the device
+# ----------------------------------------------------------------------------
+#
+# A full decode step of Gemma-4-12B attends once per layer: 48 layers, layer
+# i global iff i % 6 == 5 (8 global, 40 sliding; Model Spec "At a glance"),
+# B = 256 sequences with lengths log-uniform in [1, 131072], each layer with
+# its own inputs. That is ~66 GB of KV, too much to draw on the host, so the
+# caches are drawn on the device with torch's seeded generator (same
+# distribution as above: rows N(0, I) rescaled to RMS 1, k times the layer's
+# w_k, v unweighted, rounded to bf16 nearest-even); q, the norm weights and
+# the block tables are drawn on the host as for the other workloads. Slots no
+# query sees (past L in the last page, before the window in the first) and
+# the guard page hold NaN. The oracle is fed the stored bytes of sampled
+# sequences copied back from the device (sample_to_host).
+
+SWEEP = dict(B=256, L_max=131072, layers=48)
+STREAM_DEV_K, STREAM_DEV_V = 20, 21
+
+
+def sweep_kind(layer):
+    return "global" if layer % 6 == 5 else "sliding"
+
+
+def sweep_seq_lens(tag=(4,), B=SWEEP["B"], L_max=SWEEP["L_max"]):
+    """One length draw shared by every layer of the step (the sequences of a batch)."""
+    return loguniform_seq_lens(tag, 0, B, L_max)
+
+
+def torch_seed(tag, layer, stream):
+    ss = np.random.SeedSequence([int(t) for t in np.atleast_1d(tag)] + [int(layer), int(stream)])
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64(0x7FFFFFFFFFFFFFFF))
+
+
+@dataclass
+class DeviceLayer:
+    kind: str                  # "sliding" or "global"
+    q: object                  # torch bf16 [B, Hq, D]
+    caches: tuple              # (k_cache, v_cache) row-major, or (kv_cache,) tiled; torch bf16
+    block_table: object        # torch int32 [B, P_max]
+    seq_lens: object           # torch int32 [B]
+    host_block_table: np.ndarray
+    host_seq_lens: np.ndarray
+    host_q: np.ndarray         # stored bf16 bits [B, Hq, D]
+    window: int
+    Hkv: int
+    G: int
+    D: int
+
+
+def device_layer(kind, seq_lens, *, tag=(4,), layer=0, window=SLIDING["window"], device="cuda",
+                 chunk_pages=8192):
+    """One layer of the sweep with its caches drawn on `device`."""
+    import torch
+    shp = SLIDING if kind == "sliding" else GLOBAL
+    Hkv, G, D = shp["Hkv"], shp["G"], shp["D"]
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    B = len(seq_lens)
+    P_max = max(1, max(pages_for(L) for L in seq_lens))
+    lo_tok = np.maximum(seq_lens.astype(np.int64) - window, 0) if kind == "sliding" else np.zeros(B, np.int64)
+    ranges = [((int(lo) // PAGE, pages_for(L)) if L > 0 else (0, 0)) for lo, L in zip(lo_tok, seq_lens)]
+    bt, num_pages = build_block_table(ranges, P_max, rng_for(tag, layer, STREAM_PERM))
+    counts = np.array([hi - lo for lo, hi in ranges], dtype=np.int64)
+    owner = np.repeat(np.arange(B), counts)
+    j = np.concatenate([np.arange(lo, hi) for lo, hi in ranges]).astype(np.int64)
+    phys = bt[owner, j].astype(np.int64)                    # logical page i -> physical page
+    tok = PAGE * j[:, None] + np.arange(PAGE)[None, :]
+    visible = (tok >= lo_tok[owner][:, None]) & (tok < seq_lens[owner].astype(np.int64)[:, None])
+    n_alloc = len(phys)
+
+    w_q = norm_weight(rng_for(tag, layer, STREAM_WQ), D)
+    w_k = norm_weight(rng_for(tag, layer, STREAM_WK), D)
+    q_host = to_storage(rms_rows(rng_for(tag, layer, STREAM_Q), (B, Hkv * G, D), w_q), "bf16")
+    phys_d = torch.from_numpy(phys).to(device)
+    vis_d = torch.from_numpy(visible).to(device)
+    nan = torch.tensor(float("nan"), dtype=torch.bfloat16, device=device)
+
+    def draw(stream, weight):
+        if kind == "sliding":
+            pool = torch.empty((num_pages, Hkv, PAGE, D), dtype=torch.bfloat16, device=device)
+        else:
+            pool = torch.empty((num_pages, Hkv, D // 8, PAGE, 8), dtype=torch.bfloat16, device=device)
+        pool[num_pages - 1] = float("nan")
+        gen = torch.Generator(device=device)
+        gen.manual_seed(torch_seed(tag, layer, stream))
+        wt = None if weight is None else torch.from_numpy(np.asarray(weight, np.float32)).to(device)
+        for c0 in range(0, n_alloc, chunk_pages):
+            c1 = min(n_alloc, c0 + chunk_pages)
+            x = torch.randn((c1 - c0, PAGE, Hkv, D), generator=gen, device=device, dtype=torch.float32)
+            x = x * torch.rsqrt(x.square().mean(-1, keepdim=True) + EPS)
+            if wt is not None:
+                x = x * wt
+            x = torch.where(vis_d[c0:c1, :, None, None], x.to(torch.bfloat16), nan)
+            if kind == "sliding":
+                page = x.permute(0, 2, 1, 3)                                   # [c, Hkv, 16, D]
+            else:
+                page = x.reshape(c1 - c0, PAGE, Hkv, D // 8, 8).permute(0, 2, 3, 1, 4)  # [c, Hkv, D/8, 16, 8]
+            pool[phys_d[c0:c1]] = page
+            del x, page
+        return pool
+
+    caches = (draw(STREAM_DEV_K, w_k), draw(STREAM_DEV_V, None)) if kind == "sliding" else (draw(STREAM_DEV_K, w_k),)
+    q_dev = torch.from_numpy(q_host.view(np.int16)).to(device).view(torch.bfloat16)
+    return DeviceLayer(kind, q_dev, caches, torch.from_numpy(bt).to(device),
+                       torch.from_numpy(seq_lens).to(device), bt, seq_lens, q_host, int(window), Hkv, G, D)
+
+
+def sample_to_host(dl, rows):
+    """The stored bytes of sequences `rows` of a DeviceLayer as a host
+    workload (compact block table, NaN guard page), for the oracle."""
+    import torch
+    rows = np.asarray(rows, dtype=np.int64)
+    P_max = dl.host_block_table.shape[1]
+    picks, table = [], np.zeros((len(rows), P_max), dtype=np.int32)
+    n = 0
+    for r, b in enumerate(rows):
+        L = int(dl.host_seq_lens[b])
+        lo = max(0, L - dl.window) // PAGE if dl.kind == "sliding" else 0
+        hi = pages_for(L)
+        ids = dl.host_block_table[b, lo:hi]
+        picks.append(ids)
+        table[r, :] = -1
+        table[r, lo:hi] = np.arange(n, n + len(ids))
+        n += len(ids)
+    guard = n
+    table[table < 0] = guard
+    idx = torch.from_numpy(np.concatenate(picks + [np.array([0])]).astype(np.int64)).to(dl.block_table.device)
+
+    def take(pool):
+        got = pool[idx].cpu()
+        arr = got.view(torch.int16).numpy().view(np.uint16).copy()
+        arr[guard] = BF16_NAN
+        return arr
+
+    q = dl.host_q[rows]
+    sl = dl.host_seq_lens[rows].astype(np.int32)
+    if dl.kind == "sliding":
+        return SlidingWorkload(q, take(dl.caches[0]), take(dl.caches[1]), table, sl, dl.window, "bf16",
+                               dl.Hkv, dl.G, dl.D)
+    return GlobalWorkload(q, take(dl.caches[0]), table, sl, "bf16", dl.Hkv, dl.G, dl.D)
