@@ -89,6 +89,15 @@ __device__ __forceinline__ float sigmoidf(float x) { return 1.f / (1.f + expf(-x
 // ---------------------------------------------------------------- memory
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte load with the non-temporal hint (global_load_dwordx4 ... nt): for
+// the KV page stream, which is read once per call. Measured on gfx950, random
+// 16 KB pages stream at ~6.97 TB/s with it against ~6.15 TB/s without.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left unconstrained). Used at the end
 // of rarely taken branches that issue vector loads, so that the loads do not
 // stay pending across the join: otherwise the wait the compiler places before

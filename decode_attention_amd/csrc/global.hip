@@ -407,7 +407,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       const int phys = rfl(idv[is]);
       const size_t base = (size_t)phys * kGPageElems + lane_off;
 #pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) buf[bs][i] = ld16(a.kv + base + (size_t)i * 512);
+      for (int i = 0; i < kGKSteps; ++i) buf[bs][i] = ld16_stream(a.kv + base + (size_t)i * 512);
     };
     // One step from ring slot bs and descriptor d. Returns false for a step
     // past the range's end; the open segment is then flushed outside the

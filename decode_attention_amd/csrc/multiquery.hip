@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       r[u] = make_uint4(0u, 0u, 0u, 0u);
       if (j0 + u_pg(u) < jb) {
         const uint16_t* src = (C::kSliding && u >= 2) ? a.v : a.k;
+        // plain loads: the row blocks of a sequence re-read its pages, which
+        // the caches keep (the non-temporal hint made prefill chunks ~10% slower)
         r[u] = ld16(src + ((size_t)ph[u_pg(u)] * a.Hkv + c) * slab + c_src + u_src(u));
       }
     }

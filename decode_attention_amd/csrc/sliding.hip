@@ -129,8 +129,8 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
     const size_t base = ((size_t)phys * Hkv + c) * slab + lane_off;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kb[buf][i] = ld16(kc + base + (size_t)i * kWave * E);
-      vb[buf][i] = ld16(vc + base + (size_t)i * kWave * E);
+      kb[buf][i] = ld16_stream(kc + base + (size_t)i * kWave * E);
+      vb[buf][i] = ld16_stream(vc + base + (size_t)i * kWave * E);
     }
   };
 
