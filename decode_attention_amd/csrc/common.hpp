@@ -93,6 +93,14 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 // the KV page stream, which is read once per call. Measured on gfx950, random
 // 16 KB pages stream at ~6.97 TB/s with it against ~6.15 TB/s without.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 KB of zeros in device memory. Software pipelines that issue the same
+// loads on every pass point the slots they will not use (past the end of a
+// walk, pairs without a page) here: the lines stay in L2, where re-reading
+// the last real page with the non-temporal hint would go to HBM again.
+// A pointer select, not a branch, so the compiler's load counting is kept.
+static __device__ uint4 g_zero_page[1024];
+
 __device__ __forceinline__ uint4 ld16_stream(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);

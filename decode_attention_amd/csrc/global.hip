@@ -229,6 +229,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
   uint4 buf[kGBuf][kGKSteps];      // ring of this wave's page slices
   int idv[kGBuf];                  // physical page ids, 2 steps before their pages
+  int iduse[kGBuf];                // the pair has a page in that step (else: zero page)
   f32x4 acc[kGMTiles];             // O^T: head hq, d = 256hf + 16t + 4g + e
   float m_run = -INFINITY, l_run = 0.f;
   const size_t lane_off = (size_t)hf * kGKSteps * 512 + (size_t)lane * 8;
@@ -395,9 +396,11 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       dL[d] = gL;
       gp += n;
     };
-    // This pair's page id of step d (a past-the-end step repeats the last id).
+    // This pair's page id of step d (a past-the-end step repeats the last id;
+    // a pair without a page in the step then loads the zero page).
     auto load_id = [&](int is, int d) __attribute__((always_inline)) {
       if (dN[d] > 0) last_idx = (size_t)dB[d] * a.P_max + (size_t)(dJ[d] + min(pr, dN[d] - 1));
+      iduse[is] = PRE || pr < dN[d];  // (the pre-norm kernel, short of registers, reloads instead)
       size_t idx = last_idx;
       // a vector load: a scalar one would be waited for by every LDS wait
       asm volatile("" : "+v"(idx));
@@ -405,9 +408,10 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     };
     auto issue = [&](int bs, int is) __attribute__((always_inline)) {
       const int phys = rfl(idv[is]);
-      const size_t base = (size_t)phys * kGPageElems + lane_off;
+      const uint16_t* src = (iduse[is] ? a.kv + (size_t)phys * kGPageElems
+                                       : reinterpret_cast<const uint16_t*>(g_zero_page)) + lane_off;
 #pragma unroll
-      for (int i = 0; i < kGKSteps; ++i) buf[bs][i] = ld16_stream(a.kv + base + (size_t)i * 512);
+      for (int i = 0; i < kGKSteps; ++i) buf[bs][i] = ld16_stream(src + (size_t)i * 512);
     };
     // One step from ring slot bs and descriptor d. Returns false for a step
     // past the range's end; the open segment is then flushed outside the

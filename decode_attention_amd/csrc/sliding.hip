@@ -124,13 +124,17 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
   // page k0 + i, so no block-table load sits on the path of a page load.
   int ids = 0;
   uint4 kb[2][NI], vb[2][NI];
-  auto load = [&](int buf, int kk) {  // kk: page index inside the current chunk
+  // kk: page index inside the current chunk; a slot the loop will not
+  // compute (use = false) loads the zero page instead.
+  auto load = [&](int buf, int kk, bool use) {
     const int phys = __builtin_amdgcn_readlane(ids, kk);
-    const size_t base = ((size_t)phys * Hkv + c) * slab + lane_off;
+    const size_t base = ((size_t)phys * Hkv + c) * slab;
+    const T* kp = (use ? kc + base : reinterpret_cast<const T*>(g_zero_page)) + lane_off;
+    const T* vp = (use ? vc + base : reinterpret_cast<const T*>(g_zero_page)) + lane_off;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      kb[buf][i] = ld16_stream(kc + base + (size_t)i * kWave * E);
-      vb[buf][i] = ld16_stream(vc + base + (size_t)i * kWave * E);
+      kb[buf][i] = ld16_stream(kp + (size_t)i * kWave * E);
+      vb[buf][i] = ld16_stream(vp + (size_t)i * kWave * E);
     }
   };
 
@@ -190,18 +194,18 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
   };
 
   // Software pipeline: the next page's 16 loads are always issued before the
-  // current page is computed (clamped to the chunk's last page at the end, so
+  // current page is computed (past the chunk's end from the zero page, so
   // every pass issues the same loads and the compiler can count them).
   for (int k0 = 0; k0 < nmine; k0 += kWave) {
     const int kn = min(nmine - k0, kWave);
     ids = (k0 + lane < nmine) ? btb[j_lo + wv + NW * (k0 + lane)] : 0;
     wait_vmem_all();
-    load(0, 0);
+    load(0, 0, true);
     for (int k = 0; k < kn; k += 2) {
-      load(1, min(k + 1, kn - 1));
+      load(1, min(k + 1, kn - 1), k + 1 < kn);
       compute(0, k0 + k);
       if (k + 1 >= kn) break;
-      load(0, min(k + 2, kn - 1));
+      load(0, min(k + 2, kn - 1), k + 2 < kn);
       compute(1, k0 + k + 1);
     }
   }
