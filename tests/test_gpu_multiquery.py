@@ -169,3 +169,19 @@ def test_chunked_prefill(gpu_lib, kind):
     mq = I.make_multiquery(kind, [L, 1500], [2048, 300], tag=(908,), **shape)
     picks = [(0, j) for j in (0, 1, 63, 64, 1000, 1023, 1024, 1025, 2047)] + [(1, j) for j in (0, 150, 299)]
     sampled_check(mq, "prefill chunk 2048", picks)
+
+
+def test_balanced_split_one_long_sequence(gpu_lib):
+    # Speculative verification where one sequence holds almost every page:
+    # the default split gives that sequence's row blocks most of the grid
+    # (hundreds of pieces each, folded by the merge) and the short ones one
+    # piece each.
+    lens = np.concatenate([[100000], np.arange(1, 64) * 5])
+    mq = I.make_multiquery("global", lens, np.full(64, 8), tag=(910,), **I.GLOBAL)
+    got = run(mq)
+    assert np.isfinite(got).all()
+    for b, j in [(0, 0), (0, 7), (1, 0), (33, 5), (63, 7)]:
+        s = int(mq.q_start[b]) + j
+        err = max_abs(got[s], oracle_row(mq, b, j))
+        print(f"[multiquery] one long sequence: b={b} query {j}: max-abs {err:.3e}", flush=True)
+        assert err <= BF16_TOL
