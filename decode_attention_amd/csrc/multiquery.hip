@@ -298,8 +298,11 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   }
 }
 
-// Combines the nsplit partial slots of one row block: thread item = (row,
-// 4 coordinates), consecutive threads on consecutive coordinates.
+// Combines the nsplit partial slots of one row block. Thread item = (row, 4
+// coordinates), one item per thread: the block's items are spread over
+// kMergeChunks workgroups. The pieces are folded with a running max, 4 at a
+// time with independent loads:
+//   M = max m_i,  o = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i.
 template <int D, int G>
 __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
   using C = MQShape<D, G>;
@@ -309,30 +312,43 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
   const int S = a.q_start[b + 1] - q0;
   const int s0 = blk * C::kQueries;
   if (s0 >= S) return;
+  const int it = blockIdx.y * 256 + threadIdx.x;
+  const int r = it / (D / 4), d = (it - r * (D / 4)) * 4;
+  const int s_r = s0 + r / G;
+  if (s_r >= S) return;
   const float* base = a.ws + (size_t)(bc * a.nblk + blk) * a.nsplit * C::kSlotFloats;
-  const int Hq = a.Hkv * G;
-  for (int it = threadIdx.x; it < C::kRows * D / 4; it += 256) {
-    const int r = it / (D / 4), d = (it - r * (D / 4)) * 4;
-    const int s_r = s0 + r / G;
-    if (s_r >= S) continue;
-    float M = -INFINITY;
-    for (int k = 0; k < a.nsplit; ++k) M = fmaxf(M, base[(size_t)k * C::kSlotFloats + C::kRows * D + r]);
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    float den = 0.f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < a.nsplit; ++k) {
-        const float* sl = base + (size_t)k * C::kSlotFloats;
-        const float mk = sl[C::kRows * D + r];
-        if (mk == -INFINITY) continue;  // no key in this piece
-        const float f = exp2_fast(mk - M);
-        num += f * *reinterpret_cast<const f32x4*>(sl + (size_t)r * D + d);
-        den += f * sl[C::kRows * D + C::kRows + r];
+  float m = -INFINITY, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;
+  for (int k0 = 0; k0 < a.nsplit; k0 += U) {
+    float mi[U], li[U];
+    f32x4 ai[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      mi[u] = -INFINITY;
+      li[u] = 0.f;
+      ai[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (k0 + u < a.nsplit) {
+        const float* sl = base + (size_t)(k0 + u) * C::kSlotFloats;
+        mi[u] = sl[C::kRows * D + r];
+        li[u] = sl[C::kRows * D + C::kRows + r];
+        ai[u] = *reinterpret_cast<const f32x4*>(sl + (size_t)r * D + d);
       }
     }
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    float* op = a.out + ((size_t)(q0 + s_r) * Hq + c * G + r % G) * D + d;
-    *reinterpret_cast<f32x4*>(op) = num * inv;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (mi[u] == -INFINITY) continue;  // no key in this piece
+      const float mn = fmaxf(m, mi[u]);
+      const float fo = exp2_fast(m - mn);  // 0 when m = -inf
+      const float fi = exp2_fast(mi[u] - mn);
+      num = num * fo + ai[u] * fi;
+      den = den * fo + li[u] * fi;
+      m = mn;
+    }
   }
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  float* op = a.out + ((size_t)(q0 + s_r) * (a.Hkv * G) + c * G + r % G) * D + d;
+  *reinterpret_cast<f32x4*>(op) = num * inv;
 }
 
 template <int D, int G>
@@ -390,7 +406,10 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
     hipLaunchKernelGGL((mq_kernel<512, 16>), grid, dim3(kMThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   if (num_splits <= 1) return DA_OK;
-  const dim3 mgrid((unsigned)a.nblk, 1, (unsigned)(s.batch * s.num_kv_heads));
+  constexpr int kChunksSliding = MQShape<256, 2>::kRows * 256 / 4 / 256;
+  constexpr int kChunksGlobal = MQShape<512, 16>::kRows * 512 / 4 / 256;
+  const dim3 mgrid((unsigned)a.nblk, (unsigned)(sliding ? kChunksSliding : kChunksGlobal),
+                   (unsigned)(s.batch * s.num_kv_heads));
   if (sliding)
     hipLaunchKernelGGL((mq_merge_kernel<256, 2>), mgrid, dim3(256), 0, stream, a);
   else
