@@ -126,11 +126,10 @@ da_status multiquery(bool sliding, const void* q, const int32_t* q_start, int32_
   int dev = 0, cus = 0;
   st = current_device(&dev, &cus);
   if (st != DA_OK) return st;
-  const int splits = da::multiquery_num_splits(*shape, max_queries, window, cus);
-  const size_t need = da::multiquery_workspace_bytes(*shape, max_queries, splits);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
+  const da::mq_plan plan = da::multiquery_plan(*shape, max_queries, window, cus);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return DA_ERR_WORKSPACE;
   return da::launch_multiquery(q, q_start, max_queries, k_cache, v_cache, block_table, seq_lens, window, out,
-                               *shape, splits, workspace, (hipStream_t)stream);
+                               *shape, plan, workspace, (hipStream_t)stream);
 }
 
 }  // namespace
@@ -163,8 +162,7 @@ da_status attn_multiquery_workspace_bytes(const da_shape* shape, int32_t max_que
   int dev = 0, cus = 0;
   st = current_device(&dev, &cus);
   if (st != DA_OK) return st;
-  *bytes = da::multiquery_workspace_bytes(*shape, max_queries,
-                                          da::multiquery_num_splits(*shape, max_queries, window, cus));
+  *bytes = da::multiquery_plan(*shape, max_queries, window, cus).ws_bytes;
   return DA_OK;
 }
 

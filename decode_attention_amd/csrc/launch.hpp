@@ -33,11 +33,21 @@ da_status launch_append_global(const float* q_raw, const float* kv_raw, const fl
                                const da_shape& s, hipStream_t stream);
 
 // Several queries per sequence at its last positions (row f2).
-int multiquery_num_splits(const da_shape& s, int max_queries, int window, int num_cus);
-size_t multiquery_workspace_bytes(const da_shape& s, int max_queries, int num_splits);
+// Work layout: a fixed number of pieces per unit (sequence, KV head, row
+// block), or (balanced) pieces per unit laid out on the device from the
+// units' page counts over `grid` workgroups.
+struct mq_plan {
+  int nblk;         // row blocks per sequence
+  int units;        // batch * num_kv_heads * nblk
+  int balanced;     // 1: layout made on the device
+  int nsplit;       // fixed split: pieces per unit (1: none)
+  int grid;         // balanced: workgroups of the main kernel
+  size_t ws_bytes;  // workspace the call needs
+};
+mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_cus);
 da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queries, const void* k_cache,
                             const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                            int window, void* out, const da_shape& s, int num_splits, void* workspace,
+                            int window, void* out, const da_shape& s, const mq_plan& p, void* workspace,
                             hipStream_t stream);
 
 }  // namespace da

@@ -29,10 +29,15 @@
 // rounded values, so every output is a weighted average whose weights are
 // exact to about 2^-9 relative.
 //
-// Split over keys. When sequences x KV heads x row blocks gives too few
-// workgroups for the chip, each block's pages are divided among nsplit
+// Split over keys. When sequences x KV heads x row blocks (the units) give
+// too few workgroups for the chip, a unit's pages are divided among several
 // workgroups that write partial (acc, m, l) per row, and mq_merge_kernel
 // combines them: M = max m_i, o = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i.
+// By default the number of pieces of a unit follows its page count, so that
+// long sequences do not form the tail: mq_plan_kernel (one workgroup) lays
+// the pieces out and gives every workgroup of the main kernel a descriptor
+// (unit, piece, pieces, slot). A caller-given number of splits divides every
+// unit into that many pieces instead.
 #include <algorithm>
 
 #include "common.hpp"
@@ -47,6 +52,7 @@ constexpr int kMKSteps = kMSlice / 32;       // 16x16x32 k-steps per page and wa
 constexpr int kMTiles = kMSlice / 16;        // 16-coordinate output tiles per wave
 constexpr int kMRegion = 16384;              // LDS bytes per region of a step (2 pages of K, or of V)
 constexpr float kMRescale = 32.f;            // lazy-rescale threshold, log2 units
+constexpr int kMPlanThreads = 1024;          // one workgroup lays out a balanced split
 
 struct MQArgs {
   const uint16_t* q;        // [T][Hq][D] bf16 bits; sequence b's rows from q_start[b]
@@ -56,8 +62,13 @@ struct MQArgs {
   const int32_t* seq_lens;  // [B]
   const int32_t* q_start;   // [B + 1]
   float* out;               // [T][Hq][D]
-  float* ws;                // partial slots, [B*Hkv][nblk][nsplit][slot] (nsplit > 1)
+  float* ws;                // partial slots: [B*Hkv][nblk][nsplit][slot] (fixed split), or
+                            // [grid][slot] (balanced split)
+  int* tab;                 // balanced split: [units + 1] first slot of each unit
+  int4* desc;               // balanced split: [grid] (unit, piece, pieces, slot); unit -1: no work
   int B, Hkv, P_max, window, nblk, nsplit;
+  int balanced;             // 1: pieces per unit follow its page count
+  int units, grid;          // balanced split: B*Hkv*nblk units over `grid` workgroups
 };
 
 template <int D, int G>
@@ -74,13 +85,88 @@ struct MQShape {
 
 __device__ __forceinline__ int mq_rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Pages the rows of unit u = (sequence, KV head, row block) see, as the main
+// kernel walks them (0 for a block without rows).
+template <int D, int G>
+__device__ int mq_unit_pages(const MQArgs& a, int u) {
+  using C = MQShape<D, G>;
+  const int blk = u % a.nblk, bc = u / a.nblk, b = bc / a.Hkv;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
+  const int S = a.q_start[b + 1] - a.q_start[b];
+  const int s0 = blk * C::kQueries;
+  if (s0 >= S) return 0;
+  const int p0 = L - S + s0, p1 = L - S + min(S, s0 + C::kQueries) - 1;
+  const int klo = C::kSliding ? max(0, p0 - a.window + 1) : 0;
+  const bool any = p1 >= 0 && (!C::kSliding || a.window > 0);
+  return any ? p1 / kPage - klo / kPage + 1 : 0;
+}
+
+// Balanced split layout (one workgroup). A unit of n pages gets
+// 1 + min(floor(n (grid - units) / total), n / 8) pieces, so the pieces of all
+// units fit in the grid and hold about the same number of pages; unit u's
+// pieces are slots tab[u] .. tab[u+1]-1, and workgroup w of the main kernel
+// runs piece w - tab[u] of the unit with tab[u] <= w < tab[u+1].
+template <int D, int G>
+__global__ __launch_bounds__(kMPlanThreads) void mq_plan_kernel(MQArgs a) {
+  __shared__ long long s_sum[kMPlanThreads];
+  const int tid = threadIdx.x, U = a.units;
+  const int per = (U + kMPlanThreads - 1) / kMPlanThreads, u0 = tid * per;
+  long long loc = 0;
+  for (int u = u0; u < u0 + per && u < U; ++u) loc += mq_unit_pages<D, G>(a, u);
+  s_sum[tid] = loc;
+  __syncthreads();
+  for (int off = kMPlanThreads / 2; off > 0; off >>= 1) {
+    if (tid < off) s_sum[tid] += s_sum[tid + off];
+    __syncthreads();
+  }
+  const long long total = s_sum[0] > 0 ? s_sum[0] : 1;
+  const long long spare = a.grid > U ? a.grid - U : 0;
+  __syncthreads();
+  int cnt = 0;
+  for (int u = u0; u < u0 + per && u < U; ++u) {
+    const int n = mq_unit_pages<D, G>(a, u);
+    cnt += 1 + (int)min((long long)n * spare / total, (long long)(n / 8));
+  }
+  s_sum[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kMPlanThreads; off <<= 1) {  // inclusive scan
+    const long long v = tid >= off ? s_sum[tid - off] : 0;
+    __syncthreads();
+    s_sum[tid] += v;
+    __syncthreads();
+  }
+  int run = (int)(s_sum[tid] - cnt);
+  for (int u = u0; u < u0 + per && u < U; ++u) {
+    const int n = mq_unit_pages<D, G>(a, u);
+    const int k = 1 + (int)min((long long)n * spare / total, (long long)(n / 8));
+    a.tab[u] = run;
+    for (int i = 0; i < k; ++i) a.desc[run + i] = make_int4(u, i, k, run + i);
+    run += k;
+  }
+  if (tid == kMPlanThreads - 1) a.tab[U] = run;  // the last thread's run is the total
+  const int used = (int)s_sum[kMPlanThreads - 1];
+  for (int w = used + tid; w < a.grid; w += kMPlanThreads) a.desc[w] = make_int4(-1, 0, 1, 0);
+}
+
 template <int D, int G>
 __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) void mq_kernel(MQArgs a) {
   using C = MQShape<D, G>;
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][2 * kMRegion];
   __shared__ f32x4 s_part[2][kMWaves][kWave];  // partial S^T per page (D = 512)
 
-  const int blk = blockIdx.x, split = blockIdx.y, bc = blockIdx.z;
+  int blk = blockIdx.x, split = blockIdx.y, bc = blockIdx.z, nsplit = a.nsplit;
+  size_t slot_idx = ((size_t)bc * a.nblk + blk) * a.nsplit + split;
+  if (a.balanced) {
+    const int4 dsc = a.desc[blockIdx.x];
+    const int u = mq_rfl(dsc.x);
+    if (u < 0) return;  // no piece for this workgroup
+    blk = u % a.nblk;
+    bc = u / a.nblk;
+    split = mq_rfl(dsc.y);
+    nsplit = mq_rfl(dsc.z);
+    slot_idx = (size_t)mq_rfl(dsc.w);
+  }
   const int b = bc / a.Hkv, c = bc - b * a.Hkv;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
@@ -96,8 +182,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const bool any = khi >= 0 && (!C::kSliding || a.window > 0);
   const int jlo = any ? klo / kPage : 0;
   const int np = any ? khi / kPage - jlo + 1 : 0;
-  const int ja = jlo + (int)((long long)split * np / a.nsplit);
-  const int jb = jlo + (int)((long long)(split + 1) * np / a.nsplit);
+  const int ja = jlo + (int)((long long)split * np / nsplit);
+  const int jb = jlo + (int)((long long)(split + 1) * np / nsplit);
   const int nsteps = (jb - ja + 1) / 2;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -279,7 +365,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
   float lt = l_run + xor16(l_run);
   lt += xor32(lt);  // the row's denominator (its 4 lane groups)
-  if (a.nsplit == 1) {
+  if (nsplit == 1) {
     if (valid) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;  // nothing visible: 0
       float* op = a.out + ((size_t)(q0 + s_r) * Hq + head) * D + hf * kMSlice + 4 * g4;
@@ -287,7 +373,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       for (int t = 0; t < kMTiles; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = acc[t] * inv;
     }
   } else {
-    float* slot = a.ws + ((size_t)(bc * a.nblk + blk) * a.nsplit + split) * C::kSlotFloats;
+    float* slot = a.ws + slot_idx * C::kSlotFloats;
     float* ap = slot + (size_t)r_wg * D + hf * kMSlice + 4 * g4;
 #pragma unroll
     for (int t = 0; t < kMTiles; ++t) *reinterpret_cast<f32x4*>(ap + 16 * t) = acc[t];
@@ -316,11 +402,15 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
   const int r = it / (D / 4), d = (it - r * (D / 4)) * 4;
   const int s_r = s0 + r / G;
   if (s_r >= S) return;
-  const float* base = a.ws + (size_t)(bc * a.nblk + blk) * a.nsplit * C::kSlotFloats;
+  const int unit = bc * a.nblk + blk;
+  const int first = a.balanced ? a.tab[unit] : unit * a.nsplit;
+  const int nsplit = a.balanced ? a.tab[unit + 1] - first : a.nsplit;
+  if (nsplit <= 1) return;  // a single piece wrote its rows itself
+  const float* base = a.ws + (size_t)first * C::kSlotFloats;
   float m = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
   constexpr int U = 4;
-  for (int k0 = 0; k0 < a.nsplit; k0 += U) {
+  for (int k0 = 0; k0 < nsplit; k0 += U) {
     float mi[U], li[U];
     f32x4 ai[U];
 #pragma unroll
@@ -328,7 +418,7 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
       mi[u] = -INFINITY;
       li[u] = 0.f;
       ai[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (k0 + u < a.nsplit) {
+      if (k0 + u < nsplit) {
         const float* sl = base + (size_t)(k0 + u) * C::kSlotFloats;
         mi[u] = sl[C::kRows * D + r];
         li[u] = sl[C::kRows * D + C::kRows + r];
@@ -356,32 +446,41 @@ static int mq_blocks(int max_queries) {
   return (max_queries + MQShape<D, G>::kQueries - 1) / MQShape<D, G>::kQueries;
 }
 
-int multiquery_num_splits(const da_shape& s, int max_queries, int window, int num_cus) {
-  if (s.num_splits > 0) return s.num_splits;
-  const bool sliding = s.head_dim == 256;
-  const int nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
-  const long long base = (long long)s.batch * s.num_kv_heads * nblk;
-  // pages a block can need: the window plus the block's queries, or the row
-  const int qpb = sliding ? MQShape<256, 2>::kQueries : MQShape<512, 16>::kQueries;
-  const long long span = sliding ? std::min<long long>(s.max_pages_per_seq, (window + qpb - 1) / kPage + 2)
-                                 : s.max_pages_per_seq;
-  long long want = (2LL * num_cus + base - 1) / base;  // about two workgroups per compute unit
-  const long long cap = std::max<long long>(1, span / 8);  // at least ~4 steps per piece
-  want = std::min(want, cap);
-  return (int)std::max<long long>(1, want);
-}
+static size_t mq_align(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t multiquery_workspace_bytes(const da_shape& s, int max_queries, int num_splits) {
-  if (num_splits <= 1) return 0;
+mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_cus) {
   const bool sliding = s.head_dim == 256;
-  const int nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
-  const size_t slot = sliding ? MQShape<256, 2>::kSlotFloats : MQShape<512, 16>::kSlotFloats;
-  return (size_t)s.batch * s.num_kv_heads * nblk * (size_t)num_splits * slot * sizeof(float);
+  mq_plan p{};
+  p.nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
+  const long long units = (long long)s.batch * s.num_kv_heads * p.nblk;
+  const size_t slot = (sliding ? MQShape<256, 2>::kSlotFloats : MQShape<512, 16>::kSlotFloats) * sizeof(float);
+  // Two workgroups fit on a compute unit at a time: with fewer units than
+  // that the chip is split. A third workgroup per compute unit lets those
+  // that finish early take more pieces (measured: two or four per compute
+  // unit are slower on the verification workloads).
+  const long long target = 3LL * num_cus;
+  if (s.num_splits == 0 && units < 2LL * num_cus) {
+    // pieces per unit follow its page count, laid out on the device
+    p.balanced = 1;
+    p.nsplit = 0;
+    p.units = (int)units;
+    p.grid = (int)target;
+    const size_t desc = (size_t)p.grid * sizeof(int4), tab = (size_t)(p.units + 1) * sizeof(int);
+    p.ws_bytes = mq_align(desc) + mq_align(tab) + (size_t)p.grid * slot;
+    return p;
+  }
+  int nsplit = s.num_splits;
+  if (nsplit <= 0) nsplit = 1;  // units >= two per compute unit: no split
+  p.nsplit = nsplit;
+  p.units = (int)units;
+  p.grid = 0;
+  p.ws_bytes = nsplit > 1 ? (size_t)units * nsplit * slot : 0;
+  return p;
 }
 
 da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queries, const void* k_cache,
                             const void* v_cache, const int32_t* block_table, const int32_t* seq_lens,
-                            int window, void* out, const da_shape& s, int num_splits, void* workspace,
+                            int window, void* out, const da_shape& s, const mq_plan& p, void* workspace,
                             hipStream_t stream) {
   MQArgs a;
   a.q = (const uint16_t*)q;
@@ -391,21 +490,40 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
   a.seq_lens = seq_lens;
   a.q_start = q_start;
   a.out = (float*)out;
-  a.ws = num_splits > 1 ? (float*)workspace : nullptr;
   a.B = s.batch;
   a.Hkv = s.num_kv_heads;
   a.P_max = s.max_pages_per_seq;
   a.window = window;
-  a.nsplit = num_splits;
+  a.nblk = p.nblk;
+  a.nsplit = p.nsplit;
+  a.balanced = p.balanced;
+  a.units = p.units;
+  a.grid = p.grid;
+  a.ws = nullptr;
+  a.tab = nullptr;
+  a.desc = nullptr;
   const bool sliding = s.head_dim == 256;
-  a.nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
-  const dim3 grid((unsigned)a.nblk, (unsigned)num_splits, (unsigned)(s.batch * s.num_kv_heads));
+  dim3 grid((unsigned)a.nblk, (unsigned)a.nsplit, (unsigned)(s.batch * s.num_kv_heads));
+  if (p.balanced) {
+    uint8_t* w = (uint8_t*)workspace;
+    a.desc = (int4*)w;
+    a.tab = (int*)(w + mq_align((size_t)p.grid * sizeof(int4)));
+    a.ws = (float*)(w + mq_align((size_t)p.grid * sizeof(int4)) + mq_align((size_t)(p.units + 1) * sizeof(int)));
+    grid = dim3((unsigned)p.grid, 1, 1);
+    if (sliding)
+      hipLaunchKernelGGL((mq_plan_kernel<256, 2>), dim3(1), dim3(kMPlanThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mq_plan_kernel<512, 16>), dim3(1), dim3(kMPlanThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
+  } else if (p.nsplit > 1) {
+    a.ws = (float*)workspace;
+  }
   if (sliding)
     hipLaunchKernelGGL((mq_kernel<256, 2>), grid, dim3(kMThreads), 0, stream, a);
   else
     hipLaunchKernelGGL((mq_kernel<512, 16>), grid, dim3(kMThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
-  if (num_splits <= 1) return DA_OK;
+  if (!p.balanced && p.nsplit <= 1) return DA_OK;
   constexpr int kChunksSliding = MQShape<256, 2>::kRows * 256 / 4 / 256;
   constexpr int kChunksGlobal = MQShape<512, 16>::kRows * 512 / 4 / 256;
   const dim3 mgrid((unsigned)a.nblk, (unsigned)(sliding ? kChunksSliding : kChunksGlobal),
