@@ -121,6 +121,76 @@ def time_calls(fn, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def time_cold(fn, n, flush):
+    """Median µs of fn over n calls, each after a 1 GiB write to `flush` that
+    evicts L2 and the 256 MB Infinity Cache (events around fn only)."""
+    import numpy as np
+    import torch
+    fn()
+    times = []
+    for i in range(n):
+        flush.fill_(i & 0x7F)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+    return float(np.median(times))
+
+
+def time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, num_splits):
+    """Context for the step's numbers, timed after it: the read bandwidth the
+    kernels' access pattern reaches (HBM probe), the calls with cold caches,
+    and the long-context global call (B = 2, lengths 131072 and 262144)."""
+    import types
+    import torch
+    from decode_attention_amd import probe as P
+    res = {}
+    # probe: random 16 KB pages of a 4 GiB buffer, the decode kernels' loads
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device="cuda")
+    n_pages = buf.numel() // P.PAGE_BYTES
+    gen = torch.Generator(device="cpu").manual_seed(1234)
+    ids = torch.randperm(n_pages, generator=gen).to(torch.int32).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    best = (0.0, 0)
+    for wg in (256, 512, 1024, 2048):
+        us = time_calls(lambda: P.read_pages(buf, ids, wg, sink), 10)
+        gbs = n_pages * P.PAGE_BYTES / (us * 1e-6) / 1e9
+        res[f"hbm_probe_{wg}wg_GBps"] = round(gbs, 1)
+        best = max(best, (gbs, wg))
+    res["hbm_probe_GBps"] = round(best[0], 1)
+    res["hbm_probe_workload"] = ("4 GiB read as 16 KB pages in random order, 16-byte non-temporal loads, "
+                                 f"best of 256-2048 workgroups ({best[1]})")
+    del ids
+    flush = buf[: 1 << 30]
+    # cold caches: every call after a 1 GiB write
+    s_cold = time_cold(lambda: da.attn_decode_sliding(*d_sl[:5], sl.window, out=out_sl), 10, flush)
+    g_cold = time_cold(lambda: da.attn_decode_global(*d_gl, out=out_gl, num_splits=num_splits), 10, flush)
+    res["sliding_us_cold_median"] = round(s_cold, 2)
+    res["global_us_cold_median"] = round(g_cold, 2)
+    res["sliding_GBps_cold"] = round(sum(sb.values()) / (s_cold * 1e-6) / 1e9, 1)
+    res["global_GBps_cold"] = round(sum(gb.values()) / (g_cold * 1e-6) / 1e9, 1)
+    # long-context global layer: two sequences, 24,576 pages
+    dl = I.device_layer("global", [131072, 262144], tag=(3,))
+    out = torch.empty((2, 16, 512), dtype=torch.float32, device="cuda")
+    call = lambda: da.attn_decode_global(dl.q, *dl.caches, dl.block_table, dl.seq_lens, out=out,
+                                         num_splits=num_splits)
+    wl = types.SimpleNamespace(seq_lens=dl.host_seq_lens, window=0, kv_dtype="bf16", Hkv=1, G=16, D=512)
+    lb = sum(global_bytes(wl).values())
+    l_hot = time_calls(call, 20)
+    l_cold = time_cold(call, 10, flush)
+    res["long_context_workload"] = "global layer, B=2, seq_lens {131072, 262144}, caches drawn on the device"
+    res["long_context_us_per_call"] = round(l_hot, 2)
+    res["long_context_GBps"] = round(lb / (l_hot * 1e-6) / 1e9, 1)
+    res["long_context_us_cold_median"] = round(l_cold, 2)
+    res["long_context_GBps_cold"] = round(lb / (l_cold * 1e-6) / 1e9, 1)
+    log("context: " + ", ".join(f"{k}={v}" for k, v in res.items() if not k.endswith("workload")))
+    del dl, out, buf, flush
+    torch.cuda.empty_cache()
+    return res
+
+
 def counters_current():
     """True if the kernel sources are those the recorded counters were taken on."""
     import hashlib
@@ -349,8 +419,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the 48-call full-step sweep at B = 256 (its caches take ~80 GB of HBM)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the append and gated-call timings after the step (so that a kernel "
-                         "trace holds the step's dispatches only)")
+                    help="skip everything timed after the step (appends, gated and multi-query calls, "
+                         "HBM probe, cold-cache and long-context timings), so that a kernel trace holds "
+                         "the step's dispatches only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
@@ -404,6 +475,8 @@ def main():
     wall = time.perf_counter() - t0
     sl_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     gl_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    sl_med = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    gl_med = float(np.median([e[1].elapsed_time(e[2]) for e in evs]))
     log(f"timed: sliding {sl_ms * 1e3:.1f} us/call, global {gl_ms * 1e3:.1f} us/call, "
         f"wall {wall / args.steps * 1e3:.3f} ms/step")
 
@@ -450,6 +523,8 @@ def main():
 
     extra = {} if args.no_extras else time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb,
                                                   max(args.steps, 10), args.num_splits)
+    if not args.no_extras:
+        extra.update(time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, args.num_splits))
     if not (args.no_extras or args.no_sweep):
         extra.update(time_sweep(da, I, 5))
 
@@ -483,6 +558,8 @@ def main():
             "eager_ms_per_step": round(eager_ms, 4),
             "sliding_us_per_call": round(sl_ms * 1e3, 2),
             "global_us_per_call": round(gl_ms * 1e3, 2),
+            "sliding_us_median": round(sl_med * 1e3, 2),
+            "global_us_median": round(gl_med * 1e3, 2),
             "sliding_GBps": round(s_ach, 1),
             "global_GBps": round(g_ach, 1),
             "sliding_frac_of_peak": round(s_ach / HBM_PEAK_GBS, 4),

@@ -1,4 +1,5 @@
-"""Builds libdecode_attn.so for gfx950 with hipcc (in-tree, no JIT).
+"""Builds libdecode_attn.so (the attention library) and libdecode_attn_probe.so
+(an HBM read probe used by the benchmark) for gfx950 with hipcc, in-tree.
 
 Usage: python -m decode_attention_amd.build [--verbose]
 """
@@ -14,6 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 BUILD = os.path.join(HERE, "_build")
 SOURCES = ["api.cpp", "sliding.hip", "global.hip", "append.hip", "multiquery.hip"]
+PROBE_SOURCES = ["probe.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled for all device code.
@@ -48,19 +50,27 @@ def _compile(src, verbose, extra):
     return obj
 
 
-def build(verbose=False, extra=()):
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, list(extra)), SOURCES))
-    out = os.path.join(LIBDIR, "libdecode_attn.so")
+def _link(objs, name):
+    out = os.path.join(LIBDIR, name)
     tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError("link failed:\n" + res.stderr)
+        raise RuntimeError(f"link of {name} failed:\n" + res.stderr)
     os.replace(tmp, out)
     return out
+
+
+def build(verbose=False, extra=()):
+    """Compiles every source and links both libraries; returns the attention
+    library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose, list(extra)), srcs)))
+    _link([objs[s] for s in PROBE_SOURCES], "libdecode_attn_probe.so")
+    return _link([objs[s] for s in SOURCES], "libdecode_attn.so")
 
 
 if __name__ == "__main__":

@@ -208,3 +208,28 @@ def test_prenorm_validation(lib):
     assert call(_gshape(), ptrs=[FAKE, NULL, FAKE, FAKE, FAKE]) == -1
     assert call(_gshape(group=8)) == -2
     assert call(_gshape(kv_dtype=B.DA_DTYPE_F32)) == -2
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "decode_attn_probe.h")
+
+
+def test_probe_library_exports_and_validates():
+    from decode_attention_amd import probe as P
+    if not os.path.exists(P.probe_library_path()):
+        from decode_attention_amd.build import build
+        build()
+    plib = P.load_probe_library()
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"^\s*\w+\s+(da_probe_\w+)\s*\(", text, flags=re.M)))
+    assert declared == sorted(P.EXPORTS)
+    for name in declared:
+        assert hasattr(plib, name), name
+    f = plib.da_probe_read_pages
+    assert f(NULL, FAKE, 4, 256, FAKE, NULL) == -1
+    assert f(FAKE, NULL, 4, 256, FAKE, NULL) == -1
+    assert f(FAKE, FAKE, 4, 256, NULL, NULL) == -1
+    assert f(FAKE, FAKE, -1, 256, FAKE, NULL) == -1
+    assert f(FAKE, FAKE, 4, 0, FAKE, NULL) == -1
+    assert f(FAKE, FAKE, 4, 65536, FAKE, NULL) == -1
+    assert f(ctypes.c_void_p(0x1008), FAKE, 4, 256, FAKE, NULL) == -1  # not 16-byte aligned
+    assert f(FAKE, FAKE, 0, 256, FAKE, NULL) == 0  # nothing to read: nothing enqueued
