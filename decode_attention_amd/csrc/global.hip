@@ -135,6 +135,16 @@ __device__ __forceinline__ int range_start(int w, int N, int G) {
   return (int)(((long long)w * N) / G);
 }
 
+// floor(x / d) for 0 <= x < 2^52 and 0 < d < 2^31, through a double quotient
+// (within one of the exact one) and one correction step: a few instructions
+// where a 64-bit integer division takes dozens.
+__device__ __forceinline__ int div_floor_small(long long x, int d) {
+  long long q = (long long)((double)x / (double)d);
+  if (q * d > x) --q;
+  else if ((q + 1) * d <= x) ++q;
+  return (int)q;
+}
+
 // Sequence holding global page p (skips sequences without pages).
 __device__ __forceinline__ int seq_of_page(const int* s_pre, int B, int p) {
   int lo = 0, hi = B - 1;
@@ -625,10 +635,11 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 // Log-sum-exp merge of the partial results of split sequences. Workgroup:
 // (sequence b, output tile T = 16 coordinates of all 16 heads, i.e. one
 // lane-order tile of a partial slot); its NG groups of 64 threads fold the
-// sequence's pieces grp, grp+NG, ... with a running max, reading 1 KB
-// contiguous per piece, and are then combined the same way. The pieces are
-// found from the page prefix table in the workspace header.
-template <int NG>
+// sequence's pieces grp, grp+NG, ... with a running max, U pieces' loads in
+// flight at a time, reading 1 KB contiguous per piece, and are then combined
+// the same way. The pieces are found from the page prefix table in the
+// workspace header.
+template <int NG, int U>
 __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   constexpr int kTiles = kGPair * kGMTiles;   // 32 tiles of 16 coordinates
   __shared__ f32x4 s_num[NG][kWave];
@@ -658,7 +669,9 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
   const int N = pre[a.B];
   const int pb = pre[b], pe = pre[b + 1];
   // workgroup whose range holds page p: the largest w with range_start(w) <= p
-  auto wg_of = [&](int p) __attribute__((always_inline)) { return (int)((((long long)p + 1) * a.G - 1) / N); };
+  auto wg_of = [&](int p) __attribute__((always_inline)) {
+    return div_floor_small(((long long)p + 1) * a.G - 1, N);
+  };
   const int w0 = wg_of(pb);
   const int np = wg_of(pe - 1) - w0 + 1;  // pieces
   if (np == 1) {  // finished inside one workgroup: the row is written
@@ -669,17 +682,19 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
     }
     return;
   }
-  // slot of piece i, or -1 for an empty range
+  // slot of piece i, or -1 for an empty range. With at least as many pages
+  // as workgroups no range is empty, and only the first piece needs its
+  // range start (its workgroup may have begun in the previous sequence).
+  const bool dense = N >= a.G;
+  const int first_slot = 2 * w0 + (div_floor_small((long long)w0 * N, a.G) != pb ? 1 : 0);
   auto slot_of = [&](int i) __attribute__((always_inline)) -> int {
     const int ww = w0 + i;
-    const int rs = range_start(ww, N, a.G);
-    if (rs == range_start(ww + 1, N, a.G)) return -1;  // empty range: no piece
-    return 2 * ww + ((i == 0 && rs != pb) ? 1 : 0);
+    if (!dense && range_start(ww, N, a.G) == range_start(ww + 1, N, a.G)) return -1;  // empty range
+    return i == 0 ? first_slot : 2 * ww;
   };
   const size_t off = ((size_t)T * kWave + lane) * 4;
   float m = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;  // pieces gathered per step, loads independent
   for (int i = grp; i < np; i += U * NG) {
     float mi[U], li[U];
     f32x4 ai[U];
@@ -770,13 +785,17 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   if (num_splits <= 1) return DA_OK;  // nothing was split: no merge
   a.gate = gate;
-  // Expected pieces per sequence ~ G/B + 2: more pieces, more slot groups.
+  // Expected pieces per sequence ~ G/B + 2: more pieces, more slot groups
+  // and more loads in flight per thread, so that few rounds of dependent
+  // loads remain (one for up to 16, 64 and 192 pieces).
   const int est = num_splits / s.batch + 2;
   const unsigned nb = (unsigned)s.batch * (kGPair * kGMTiles);
-  if (est <= 24)
-    hipLaunchKernelGGL(lse_merge_kernel<4>, dim3(nb), dim3(4 * kWave), 0, stream, a);
+  if (est <= 16)
+    hipLaunchKernelGGL((lse_merge_kernel<4, 4>), dim3(nb), dim3(4 * kWave), 0, stream, a);
+  else if (est <= 64)
+    hipLaunchKernelGGL((lse_merge_kernel<16, 4>), dim3(nb), dim3(16 * kWave), 0, stream, a);
   else
-    hipLaunchKernelGGL(lse_merge_kernel<16>, dim3(nb), dim3(16 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<16, 12>), dim3(nb), dim3(16 * kWave), 0, stream, a);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
