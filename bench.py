@@ -153,9 +153,10 @@ def time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, num_splits):
     gen = torch.Generator(device="cpu").manual_seed(1234)
     ids = torch.randperm(n_pages, generator=gen).to(torch.int32).cuda()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.read_pages(buf, ids, 256, sink)  # checks the ids once
     best = (0.0, 0)
     for wg in (256, 512, 1024, 2048):
-        us = time_calls(lambda: P.read_pages(buf, ids, wg, sink), 10)
+        us = time_calls(lambda: P.read_pages(buf, ids, wg, sink, check_ids=False), 10)
         gbs = n_pages * P.PAGE_BYTES / (us * 1e-6) / 1e9
         res[f"hbm_probe_{wg}wg_GBps"] = round(gbs, 1)
         best = max(best, (gbs, wg))

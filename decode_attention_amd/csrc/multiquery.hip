@@ -211,30 +211,34 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   // tokens][8], thread tid taking chunk tid >> 4 of token tid & 15. Global:
   // the tiled page [64 chunks][16 tokens][8] is copied as it is, chunk
   // (u & 1) * 512 + tid of page u >> 1.
+  // In LDS, token j of an odd chunk sits in slot (j + 4) mod 16: each 16-lane
+  // quarter of a transposed V^T read then takes 64 bytes of chunk 2t and 64
+  // bytes of chunk 2t+1 from different halves of the 32 banks.
   const int c_tok = tid & 15;
   const int c_src = C::kSliding ? (tid & 15) * 256 + (tid >> 4) * 8 : tid * 8;  // + u-dependent part
-  const int c_lds = C::kSliding ? ((tid >> 4) * 16 + (tid & 15)) * 16 : tid * 16;
+  const int c_lds = (tid >> 4) * 256 + (((tid & 15) + ((tid >> 4) & 1) * 4) & 15) * 16;
   auto u_pg = [](int u) constexpr { return C::kSliding ? (u & 1) : (u >> 1); };
   auto u_src = [](int u) constexpr { return C::kSliding ? 0 : (u & 1) * kMThreads * 8; };
   auto u_lds = [](int u) constexpr {
     return C::kSliding ? (u >> 1) * kMRegion + (u & 1) * C::kKPage : (u >> 1) * C::kKPage + (u & 1) * kMThreads * 16;
   };
   const size_t slab = (size_t)kPage * D;
+  // Every step issues the same loads: pages past the piece's end read the
+  // zero page instead (selected, not branched around, so that the compiler
+  // keeps counting the loads in flight and waits only for the step it needs).
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_page);
   auto load_step = [&](int k, uint4(&r)[4]) __attribute__((always_inline)) {
     const int j0 = ja + 2 * k;
-    int ph[2] = {0, 0};
+    int ph[2];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg)
-      if (j0 + pg < jb) ph[pg] = a.bt[(size_t)b * a.P_max + j0 + pg];
+    for (int pg = 0; pg < 2; ++pg) ph[pg] = a.bt[(size_t)b * a.P_max + min(j0 + pg, jb - 1)];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      r[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (j0 + u_pg(u) < jb) {
-        const uint16_t* src = (C::kSliding && u >= 2) ? a.v : a.k;
-        // plain loads: the row blocks of a sequence re-read its pages, which
-        // the caches keep (the non-temporal hint made prefill chunks ~10% slower)
-        r[u] = ld16(src + ((size_t)ph[u_pg(u)] * a.Hkv + c) * slab + c_src + u_src(u));
-      }
+      const uint16_t* src = (C::kSliding && u >= 2) ? a.v : a.k;
+      const uint16_t* pgp = j0 + u_pg(u) < jb ? src + ((size_t)ph[u_pg(u)] * a.Hkv + c) * slab : zero;
+      // plain loads: the row blocks of a sequence re-read its pages, which
+      // the caches keep (the non-temporal hint made prefill chunks ~10% slower)
+      r[u] = ld16(pgp + c_src + u_src(u));
     }
   };
   // Tokens no row of the block sees (and pages of other splits) are stored
@@ -255,14 +259,19 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   for (int t = 0; t < kMTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const int s16 = lane & 15;
-  const int tr_off = ((s16 & 3) >> 1) * 256 + (4 * g4 + (s16 >> 2)) * 16 + (s16 & 1) * 8;
+  // K (A operand): chunk lane >> 4 of a 4-chunk group, token lane & 15.
+  const int k_off = (lane >> 4) * 256 + (((lane & 15) + ((lane >> 4) & 1) * 4) & 15) * 16;
+  // V^T (transposed reads): chunk (s16 & 3) >> 1 of the tile's two, token
+  // 4 g4 + (s16 >> 2), 8-byte half s16 & 1.
+  const int tr_ch = (s16 & 3) >> 1;
+  const int tr_off = tr_ch * 256 + (((4 * g4 + (s16 >> 2)) + tr_ch * 4) & 15) * 16 + (s16 & 1) * 8;
 
   auto compute = [&](int k, int buf) __attribute__((always_inline)) {
     const int j0 = ja + 2 * k;
     f32x4 sp[2];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
-      const uint8_t* kp = &s_kv[buf][pg * C::kKPage + hf * 8192 + lane * 16];
+      const uint8_t* kp = &s_kv[buf][pg * C::kKPage + hf * 8192 + k_off];
       f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       constexpr int kKB = 4;  // k-steps per batch of LDS reads
 #pragma unroll
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       l_run += (float)pp[e];
     }
     const uint8_t* vb = &s_kv[buf][C::kVBase + hf * 8192];
-    constexpr int kVB = 4;  // tiles per batch of transposed reads
+    constexpr int kVB = 2;  // tiles per batch of transposed reads (4 spills registers)
 #pragma unroll
     for (int t0 = 0; t0 < kMTiles; t0 += kVB) {
       s16x4 v0[kVB], v1[kVB];
@@ -349,13 +358,15 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     load_step(2, ra);
     __syncthreads();
     // Step k computes from buffer k % 2 while the registers hold steps k + 1
-    // and k + 2; loads past the last step are predicated off (zeros).
+    // and k + 2. The loop runs an even number of steps: a step past the last
+    // one holds zeros and no visible token, so it adds nothing (a loop exit
+    // between the two halves made the compiler wait for every load in
+    // flight in the first half).
     for (int k = 0; k < nsteps; k += 2) {
       compute(k, 0);
       store_step(k + 1, rb2, 1);
       load_step(k + 3, rb2);
       __syncthreads();
-      if (k + 1 >= nsteps) break;
       compute(k + 1, 1);
       store_step(k + 2, ra, 0);
       load_step(k + 4, ra);

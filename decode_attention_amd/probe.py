@@ -39,9 +39,11 @@ def load_probe_library():
         return lib
 
 
-def read_pages(buf, page_ids, workgroups, sink, stream=None):
+def read_pages(buf, page_ids, workgroups, sink, stream=None, check_ids=True):
     """Reads the 16 KB pages of `buf` (a cuda tensor) that `page_ids` (cuda
-    int32) lists, in that order, on the current stream."""
+    int32) lists, in that order, on the current stream. check_ids=False
+    skips the range check of the ids (a device reduction and a host sync per
+    call): for timing loops over ids already checked once."""
     import torch
     if not (buf.is_cuda and buf.is_contiguous()):
         raise ValueError("buf must be a contiguous cuda tensor")
@@ -53,9 +55,10 @@ def read_pages(buf, page_ids, workgroups, sink, stream=None):
     n_pages = buf.numel() * buf.element_size() // PAGE_BYTES
     if page_ids.numel() == 0:
         return  # nothing to read (an empty tensor has no device address to pass)
-    lo, hi = int(page_ids.min()), int(page_ids.max())
-    if lo < 0 or hi >= n_pages:
-        raise ValueError(f"page ids must lie in [0, {n_pages})")
+    if check_ids:
+        lo, hi = int(page_ids.min()), int(page_ids.max())
+        if lo < 0 or hi >= n_pages:
+            raise ValueError(f"page ids must lie in [0, {n_pages})")
     _check(load_probe_library().da_probe_read_pages(
         ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(page_ids.data_ptr()), int(page_ids.numel()),
         int(workgroups), ctypes.c_void_p(sink.data_ptr()), _stream(stream)))
