@@ -209,14 +209,17 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   // Chunk u (0..3) of 16 bytes per step and thread. Sliding: u = 2 * (V) +
   // page; the row-major slab [16 tokens][256] is stored as [32 chunks][16
   // tokens][8], thread tid taking chunk tid >> 4 of token tid & 15. Global:
-  // the tiled page [64 chunks][16 tokens][8] is copied as it is, chunk
-  // (u & 1) * 512 + tid of page u >> 1.
-  // In LDS, token j of an odd chunk sits in slot (j + 4) mod 16: each 16-lane
-  // quarter of a transposed V^T read then takes 64 bytes of chunk 2t and 64
-  // bytes of chunk 2t+1 from different halves of the 32 banks.
+  // the tiled page [64 chunks][16 tokens][8] is read 16 bytes per thread,
+  // chunk ((u & 1) * 512 + tid) >> 4 of page u >> 1, token tid & 15.
+  // LDS layout of a page: chunks in pairs (2p, 2p+1) of 512 bytes, each pair
+  // as [tokens 0-7 of 2p][tokens 0-7 of 2p+1][tokens 8-15 of 2p][tokens 8-15
+  // of 2p+1], 16 bytes per token. The page stores (16 bytes per thread), the
+  // K reads and the transposed V^T reads are then all free of bank conflicts
+  // (the plain [chunk][token] order costs the transposed reads 2 extra cycles
+  // each).
   const int c_tok = tid & 15;
   const int c_src = C::kSliding ? (tid & 15) * 256 + (tid >> 4) * 8 : tid * 8;  // + u-dependent part
-  const int c_lds = (tid >> 4) * 256 + (((tid & 15) + ((tid >> 4) & 1) * 4) & 15) * 16;
+  const int c_lds = (tid >> 5) * 512 + (((tid & 15) >> 3) * 2 + ((tid >> 4) & 1)) * 128 + (tid & 7) * 16;
   auto u_pg = [](int u) constexpr { return C::kSliding ? (u & 1) : (u >> 1); };
   auto u_src = [](int u) constexpr { return C::kSliding ? 0 : (u & 1) * kMThreads * 8; };
   auto u_lds = [](int u) constexpr {
@@ -260,11 +263,12 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   float m_run = -INFINITY, l_run = 0.f;
   const int s16 = lane & 15;
   // K (A operand): chunk lane >> 4 of a 4-chunk group, token lane & 15.
-  const int k_off = (lane >> 4) * 256 + (((lane & 15) + ((lane >> 4) & 1) * 4) & 15) * 16;
+  const int k_off = (lane >> 5) * 512 + (((lane & 15) >> 3) * 2 + ((lane >> 4) & 1)) * 128 + (lane & 7) * 16;
   // V^T (transposed reads): chunk (s16 & 3) >> 1 of the tile's two, token
   // 4 g4 + (s16 >> 2), 8-byte half s16 & 1.
   const int tr_ch = (s16 & 3) >> 1;
-  const int tr_off = tr_ch * 256 + (((4 * g4 + (s16 >> 2)) + tr_ch * 4) & 15) * 16 + (s16 & 1) * 8;
+  const int tr_tok = 4 * g4 + (s16 >> 2);
+  const int tr_off = ((tr_tok >> 3) * 2 + tr_ch) * 128 + (tr_tok & 7) * 16 + (s16 & 1) * 8;
 
   auto compute = [&](int k, int buf) __attribute__((always_inline)) {
     const int j0 = ja + 2 * k;
