@@ -469,10 +469,12 @@ mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_
   p.nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
   const long long units = (long long)s.batch * s.num_kv_heads * p.nblk;
   const size_t slot = (sliding ? MQShape<256, 2>::kSlotFloats : MQShape<512, 16>::kSlotFloats) * sizeof(float);
-  // Two workgroups fit on a compute unit at a time: with fewer units than
-  // that the chip is split. A third workgroup per compute unit lets those
-  // that finish early take more pieces (measured: two or four per compute
-  // unit are slower on the verification workloads).
+  // One workgroup runs on a compute unit at a time (8 waves of ~190 VGPRs).
+  // With fewer than two units per compute unit the keys are split, into
+  // three pieces' worth per compute unit: the dispatcher hands the later
+  // pieces to the compute units that finish first (measured on the
+  // verification workloads: 3 and 4 per compute unit best, 1, 2 and 6
+  // slower).
   const long long target = 3LL * num_cus;
   if (s.num_splits == 0 && units < 2LL * num_cus) {
     // pieces per unit follow its page count, laid out on the device
