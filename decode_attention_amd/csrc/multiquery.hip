@@ -270,11 +270,17 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const int tr_tok = 4 * g4 + (s16 >> 2);
   const int tr_off = ((tr_tok >> 3) * 2 + tr_ch) * 128 + (tr_tok & 7) * 16 + (s16 & 1) * 8;
 
+  // A wave whose 16 rows hold no query of the block (few queries per
+  // sequence: speculative verification on sliding layers fills one wave of
+  // eight) takes part in the loads and barriers only.
+  const bool wact = s0 + (rb * 16) / G <= s1;
+
   auto compute = [&](int k, int buf) __attribute__((always_inline)) {
     const int j0 = ja + 2 * k;
-    f32x4 sp[2];
+    f32x4 sp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
+      if (!wact) break;
       const uint8_t* kp = &s_kv[buf][pg * C::kKPage + hf * 8192 + k_off];
       f32x4 x[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       constexpr int kKB = 4;  // k-steps per batch of LDS reads
@@ -298,6 +304,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       sp[0] = s_part[0][wv & ~1][lane] + s_part[0][wv | 1][lane];
       sp[1] = s_part[1][wv & ~1][lane] + s_part[1][wv | 1][lane];
     }
+    if (!wact) return;
     float sc[8];
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg)
