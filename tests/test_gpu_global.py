@@ -112,3 +112,29 @@ def test_config2_full_size_sampled(gpu_lib):
 def test_config3_long_context(gpu_lib):
     wl = I.config_workload(3)
     check(wl, "config 3")
+
+
+@pytest.mark.parametrize("num_splits", [0, 5])
+def test_page_permutation_invariant_and_read_only(gpu_lib, num_splits):
+    """Re-placing the pages (block table updated to match) gives the same
+    output bit for bit, and the call leaves the cache as it found it."""
+    import torch
+
+    import decode_attention_amd as da
+    a = I.make_global([1, 300, 5000, 16, 2049, 777], kv_dtype="bf16", tag=(230,), **I.GLOBAL)
+    q, kv = dev(a.q), dev(a.kv_cache)
+    bt, sl = dev(a.block_table), dev(a.seq_lens)
+    ksum = kv.view(torch.int16).to(torch.int64).sum().item()
+    o1 = da.attn_decode_global(q, kv, bt, sl, num_splits=num_splits).cpu()
+    torch.cuda.synchronize()
+    assert kv.view(torch.int16).to(torch.int64).sum().item() == ksum
+    guard = a.meta["num_pages"] - 1
+    perm = np.random.default_rng(8).permutation(guard)
+    kv2 = a.kv_cache.copy()
+    kv2[perm] = a.kv_cache[:-1]
+    bt2 = a.block_table.copy()
+    used = bt2 != guard
+    bt2[used] = perm[bt2[used]]
+    print(f"[global] permuted placement: splits={num_splits} pages={guard}", flush=True)
+    o2 = da.attn_decode_global(q, dev(kv2), dev(bt2), sl, num_splits=num_splits).cpu()
+    assert torch.equal(o1, o2)

@@ -1,9 +1,10 @@
 """A decode step captured into a HIP graph (how a serving loop replays it):
 every replay must reproduce the eager outputs, with eager work and
 synchronisations between replays. The calls record kernel launches only (no
-memset nodes). With a fixed split the kernels are deterministic, so replays
-match bit for bit; the default global split sizes its ranges from weights
-kept in its (per-stream) workspace, so it matches to fp32 rounding."""
+memset nodes). The global split depends only on the lengths and the number
+of workgroups (one per compute unit by default, or the caller's count), and
+the merge folds pieces in a fixed order, so every replay matches the eager
+outputs bit for bit, also with the workspace of another stream."""
 
 import numpy as np
 import pytest
@@ -56,4 +57,4 @@ def test_graph_replays_match_eager(gpu_lib):
         print(f"[graph] replay {replay}", flush=True)
         assert np.array_equal(o_sl.cpu().numpy(), ref_sl), replay
         assert np.array_equal(o_gl.cpu().numpy(), ref_gl), replay
-        assert float(np.max(np.abs(o_gd.cpu().numpy() - ref_gd))) <= 2e-4, replay
+        assert np.array_equal(o_gd.cpu().numpy(), ref_gd), replay
