@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     attn_decode_global_prenorm,
     attn_kv_append_sliding,
     attn_kv_append_global,
+    attn_kv_append_global_prenorm,
     attn_multiquery_sliding,
     attn_multiquery_global,
     attn_multiquery_workspace_bytes,

@@ -45,7 +45,7 @@ class DaShape(ctypes.Structure):
 
 EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
            "attn_decode_sliding_gated", "attn_decode_global_gated", "attn_decode_global_prenorm",
-           "attn_kv_append_sliding", "attn_kv_append_global",
+           "attn_kv_append_sliding", "attn_kv_append_global", "attn_kv_append_global_prenorm",
            "attn_multiquery_sliding", "attn_multiquery_global", "attn_multiquery_workspace_bytes",
            "attn_status_string")
 
@@ -88,6 +88,8 @@ def load_library():
         lib.attn_kv_append_sliding.restype = ctypes.c_int32
         lib.attn_kv_append_global.argtypes = [vp] * 8 + [ctypes.POINTER(DaShape), vp]
         lib.attn_kv_append_global.restype = ctypes.c_int32
+        lib.attn_kv_append_global_prenorm.argtypes = [vp] * 7 + [ctypes.POINTER(DaShape), vp]
+        lib.attn_kv_append_global_prenorm.restype = ctypes.c_int32
         lib.attn_multiquery_sliding.argtypes = [vp, vp, ctypes.c_int32, vp, vp, vp, vp, ctypes.c_int32, vp,
                                                 ctypes.POINTER(DaShape), vp, ctypes.c_size_t, vp]
         lib.attn_multiquery_sliding.restype = ctypes.c_int32
@@ -352,6 +354,39 @@ def attn_kv_append_global(q_raw, kv_raw, w_q, w_k, block_table, positions, kv_ca
     _check(lib.attn_kv_append_global(_ptr(q_raw), _ptr(kv_raw), _ptr(w_q), _ptr(w_k), _ptr(block_table),
                                      _ptr(positions), _ptr(kv_cache), _ptr(q_out), ctypes.byref(shape),
                                      _stream(stream)))
+    return q_out
+
+
+def attn_kv_append_global_prenorm(q_raw, x_raw, w_q, block_table, positions, x_cache, q_out=None, stream=None):
+    """Norm + RoPE of the new tokens' q of a global layer, and the append of
+    their shared projection x, unnormalised, to the bf16 pre-norm cache
+    [P, Hkv, 64, 16, 8] that attn_decode_global_prenorm reads: q_raw fp32
+    [B, Hq, 512], x_raw fp32 [B, Hkv, 512], w_q fp32 [512], positions int32
+    [B]; returns q_out bf16 [B, Hq, 512]."""
+    import torch
+    lib = load_library()
+    _require(x_cache.dim() == 5 and x_cache.dtype == torch.bfloat16 and tuple(x_cache.shape[2:]) == (64, PAGE_SIZE, 8)
+             and x_cache.is_contiguous() and x_cache.is_cuda, "x_cache must be contiguous bf16 [P, Hkv, 64, 16, 8]")
+    P, Hkv = x_cache.shape[0], x_cache.shape[1]
+    D = 512
+    B, Hq = q_raw.shape[0], q_raw.shape[1]
+    dev = x_cache.device
+    _check_f32("q_raw", q_raw, (B, Hq, D), dev)
+    _check_f32("x_raw", x_raw, (B, Hkv, D), dev)
+    _check_f32("w_q", w_q, (D,), dev)
+    _require(Hq % Hkv == 0, "head shape mismatch")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous()
+             and block_table.shape[0] == B and block_table.device == dev, "block_table must be int32 [B, P_max]")
+    _require(positions.dtype == torch.int32 and tuple(positions.shape) == (B,) and positions.is_contiguous()
+             and positions.device == dev, "positions must be int32 [B]")
+    if q_out is None:
+        q_out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _require(q_out.dtype == torch.bfloat16 and q_out.is_contiguous() and tuple(q_out.shape) == (B, Hq, D),
+             "q_out must be contiguous bf16 [B, Hq, D]")
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, DA_DTYPE_BF16)
+    _check(lib.attn_kv_append_global_prenorm(_ptr(q_raw), _ptr(x_raw), _ptr(w_q), _ptr(block_table),
+                                             _ptr(positions), _ptr(x_cache), _ptr(q_out), ctypes.byref(shape),
+                                             _stream(stream)))
     return q_out
 
 

@@ -247,6 +247,21 @@ da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const f
                                   (hipStream_t)stream);
 }
 
+da_status attn_kv_append_global_prenorm(const float* q_raw, const float* x_raw, const float* w_q,
+                                        const int32_t* block_table, const int32_t* positions, void* x_cache,
+                                        void* q_out, const da_shape* shape, void* stream) {
+  da_status st = check_common(shape);
+  if (st != DA_OK) return st;
+  if (!q_raw || !x_raw || !w_q || !block_table || !positions || !x_cache || !q_out) return DA_ERR_INVALID_ARG;
+  if (shape->head_dim != 512 || shape->kv_dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;
+  if ((long long)shape->batch * shape->num_kv_heads * (shape->group + 1) > 0x7FFFFFFFLL) return DA_ERR_UNSUPPORTED;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  return da::launch_append_global_prenorm(q_raw, x_raw, w_q, block_table, positions, x_cache, q_out, *shape,
+                                          (hipStream_t)stream);
+}
+
 const char* attn_status_string(da_status status) {
   switch (status) {
     case DA_OK: return "ok";

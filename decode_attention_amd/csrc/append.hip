@@ -58,9 +58,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // T: cache and q_out element type; D: head dim; SEP: separate k and v caches
-// (row-major pages) rather than one K=V cache (tiled pages).
-template <typename T, int D, bool SEP>
+// (row-major pages) rather than one K=V cache (tiled pages). PRE (global
+// layers, bf16): the cache keeps the pre-norm projection x of each token,
+// which the pre-norm decode normalises and rotates itself, so the k row is
+// stored as it comes, in that cache's layout: coordinate d of block
+// B = d / 32 goes to chunk 32 (B % 2) + 4 (B / 2) + (d / 8) % 4, element d % 8
+// ([P][Hkv][64][16][8]).
+template <typename T, int D, bool SEP, bool PRE = false>
 __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendArgs a) {
+  static_assert(!PRE || (D == 512 && !SEP), "pre-norm cache: global layers");
   constexpr int J = D / kWave;       // coordinates per lane
   constexpr int JH = J / 2;          // pairs per lane
   constexpr int X = 16 / sizeof(T);  // elements per 16-byte chunk of a tiled page
@@ -86,11 +92,14 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendA
     ss = fmaf(y[j], y[j], ss);
   }
   const float inv = 1.f / sqrtf(wave_sum(ss) / (float)D + kAppendEps);
+  const bool raw = PRE && is_k;  // stored as the pre-norm projection
   const float* w = is_q ? a.w_q : (is_k ? a.w_k : nullptr);
+  if (!raw) {
 #pragma unroll
-  for (int j = 0; j < J; ++j) y[j] = y[j] * inv * (w ? w[lane + kWave * j] : 1.f);
+    for (int j = 0; j < J; ++j) y[j] = y[j] * inv * (w ? w[lane + kWave * j] : 1.f);
+  }
 
-  if (is_q || is_k) {  // rotate pairs (i, i + D/2), i = lane + 64j
+  if (is_q || (is_k && !raw)) {  // rotate pairs (i, i + D/2), i = lane + 64j
 #pragma unroll
     for (int j = 0; j < JH; ++j) {
       const int i = lane + kWave * j;
@@ -118,6 +127,9 @@ __global__ __launch_bounds__(kAppendWaves * kWave) void kv_append_kernel(AppendA
     size_t off;
     if constexpr (SEP)
       off = ((page * a.Hkv + c) * kPage + slot) * D + d;  // [P][Hkv][16][D]
+    else if constexpr (PRE)
+      off = (((page * a.Hkv + c) * (D / X) + 32 * ((d >> 5) & 1) + 4 * (d >> 6) + ((d >> 3) & 3)) * kPage + slot) * X +
+            (d & 7);  // [P][Hkv][64][16][8], pre-norm chunk order
     else
       off = (((page * a.Hkv + c) * (D / X) + d / X) * kPage + slot) * X + d % X;  // [P][Hkv][D/X][16][X]
     cache[off] = store_cast<T>(y[j]);
@@ -150,6 +162,18 @@ da_status launch_append_sliding(const float* q_raw, const float* k_raw, const fl
   AppendArgs a = {q_raw, k_raw, v_raw, w_q, w_k, block_table, positions, k_cache, v_cache, q_out,
                   s.batch, s.num_kv_heads, s.group, s.max_pages_per_seq, 10000.0, 256, 128};
   return run_append(a, s.head_dim, true, s.kv_dtype, stream);
+}
+
+da_status launch_append_global_prenorm(const float* q_raw, const float* x_raw, const float* w_q,
+                                       const int32_t* block_table, const int32_t* positions, void* x_cache,
+                                       void* q_out, const da_shape& s, hipStream_t stream) {
+  if (s.head_dim != 512 || s.kv_dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;
+  const AppendArgs a = {q_raw, x_raw, nullptr, w_q, nullptr, block_table, positions, x_cache, nullptr, q_out,
+                        s.batch, s.num_kv_heads, s.group, s.max_pages_per_seq, 1000000.0, 512, 64};
+  const long long tasks = (long long)a.B * (a.Hkv * a.G + a.Hkv);
+  const dim3 grid((unsigned)((tasks + kAppendWaves - 1) / kAppendWaves)), block(kAppendWaves * kWave);
+  hipLaunchKernelGGL((kv_append_kernel<uint16_t, 512, false, true>), grid, block, 0, stream, a);
+  return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
 da_status launch_append_global(const float* q_raw, const float* kv_raw, const float* w_q, const float* w_k,

@@ -31,6 +31,11 @@ da_status launch_append_sliding(const float* q_raw, const float* k_raw, const fl
 da_status launch_append_global(const float* q_raw, const float* kv_raw, const float* w_q, const float* w_k,
                                const int32_t* block_table, const int32_t* positions, void* kv_cache, void* q_out,
                                const da_shape& s, hipStream_t stream);
+// The same for the pre-norm cache of the global layers: q as above, the new
+// token's projection stored unnormalised and unrotated.
+da_status launch_append_global_prenorm(const float* q_raw, const float* x_raw, const float* w_q,
+                                       const int32_t* block_table, const int32_t* positions, void* x_cache,
+                                       void* q_out, const da_shape& s, hipStream_t stream);
 
 // Several queries per sequence at its last positions (row f2).
 // Work layout: a fixed number of pieces per unit (sequence, KV head, row

@@ -230,6 +230,27 @@ da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const f
                                 const float* w_k, const int32_t* block_table, const int32_t* positions,
                                 void* kv_cache, void* q_out, const da_shape* shape, void* stream);
 
+/*
+ * The decode-step append for the pre-norm cache of the global layers (the
+ * cache attn_decode_global_prenorm reads): q as in attn_kv_append_global
+ * (rmsnorm with w_q, then RoPE, theta 10^6, 64 active frequencies; Op Specs
+ * Norm.lean and Rope.lean, Model Spec attn.qk_norm and attn.rope), and the
+ * new token's shared projection x stored as it comes, rounded to bf16, in
+ * slot positions[b] % 16 of page block_table[b][positions[b] / 16] of
+ * x_cache [P][Hkv][64][16][8] (coordinate d of 32-wide block B = d / 32 in
+ * chunk 32 (B % 2) + 4 (B / 2) + (d / 8) % 4, element d % 8). The k-norm
+ * weight and the rotation of k are applied by the decode.
+ *
+ *   q_raw : fp32 [batch][Hkv*G][512];  x_raw : fp32 [batch][Hkv][512];
+ *   w_q   : fp32 [512];  x_cache : bf16 pre-norm pages;  q_out : bf16
+ *   [batch][Hkv*G][512]. shape: head_dim 512, kv_dtype BF16. Positions,
+ *   block table, ownership, errors and asynchrony as for
+ *   attn_kv_append_global.
+ */
+da_status attn_kv_append_global_prenorm(const float* q_raw, const float* x_raw, const float* w_q,
+                                        const int32_t* block_table, const int32_t* positions, void* x_cache,
+                                        void* q_out, const da_shape* shape, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 /*
  * Several queries per sequence (chunked prefill, speculative verification):

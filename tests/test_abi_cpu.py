@@ -136,10 +136,28 @@ def test_append_validation(lib):
     assert append_global(lib, s) == -2
 
 
+def append_prenorm(lib, shape, ptrs=None):
+    p = ptrs or [FAKE] * 7
+    return lib.attn_kv_append_global_prenorm(*p, ctypes.byref(shape) if shape is not None else None, NULL)
+
+
+def test_append_prenorm_validation(lib):
+    assert append_prenorm(lib, None) == -1
+    for i in range(7):  # every pointer argument is required
+        ptrs = [FAKE] * 7
+        ptrs[i] = NULL
+        assert append_prenorm(lib, _gshape(), ptrs=ptrs) == -1
+    assert append_prenorm(lib, _gshape(head_dim=256)) == -2
+    s = _gshape()
+    s.kv_dtype = B.DA_DTYPE_F32  # the pre-norm cache is bf16 only
+    assert append_prenorm(lib, s) == -2
+
+
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
 def test_append_no_device_reported_after_valid_arguments(lib):
     assert append_sliding(lib, _shape()) == -4
     assert append_global(lib, _gshape()) == -4
+    assert append_prenorm(lib, _gshape()) == -4
 
 
 def sliding_gated(lib, shape, gate=FAKE, ptrs=None):

@@ -85,3 +85,41 @@ def test_full_size_sampled(gpu_lib):
     order = np.argsort(sl)
     rows = np.unique(np.concatenate([order[:2], order[-2:], [0, 31]]))
     check(wl, "B=64 U[1,32768]", rows=rows)
+
+
+def test_append_into_prenorm_cache_then_decode(gpu_lib):
+    """attn_kv_append_global_prenorm: q as the oracle's decode-step q (within
+    one bf16 ulp), the new token's projection stored as bf16(x) in its slot of
+    the pre-norm layout with every other byte of the cache unchanged, and the
+    pre-norm decode over the appended cache against the oracle."""
+    L = np.array([0, 15, 16, 17, 300, 4095], dtype=np.int32)  # new token at position L
+    wl = I.make_global_prenorm(L + 1, tag=(960,))               # pages with room for it
+    B, Hq, D = len(L), 16, 512
+    rng = np.random.default_rng(961)
+    q_raw = (rng.standard_normal((B, Hq, D)) * 2.0).astype(np.float32)
+    x_raw = (rng.standard_normal((B, 1, D)) * 3.0).astype(np.float32)
+    w_q = (1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    print(f"[prenorm append] B={B} positions={list(L)}", flush=True)
+    xc = dev(wl.x_cache)
+    q_out = da.attn_kv_append_global_prenorm(dev(q_raw), dev(x_raw), dev(w_q), dev(wl.block_table), dev(L), xc)
+    torch.cuda.synchronize()
+    q_bits = q_out.cpu().view(torch.int16).numpy().view(np.uint16)
+    cache = xc.cpu().view(torch.int16).numpy().view(np.uint16)
+
+    q_ref, _ = oracle.decode_step_qk_global(q_raw.astype(np.float64), x_raw.astype(np.float64),
+                                            w_q.astype(np.float64), w_q.astype(np.float64), L)
+    got_q = oracle.stored_to_f64(q_bits, "bf16")
+    ulp = np.abs(got_q) * 2.0 ** -7 + 1e-30
+    assert (np.abs(got_q - q_ref) <= np.maximum(ulp, np.abs(q_ref) * 2.0 ** -7)).all()
+
+    expected = wl.x_cache.copy()
+    for b in range(B):
+        I.scatter_prenorm(expected, wl.block_table[b], [int(L[b])], I.to_storage(x_raw[b:b + 1].astype(np.float64), "bf16"))
+    np.testing.assert_array_equal(cache, expected)
+
+    o = da.attn_decode_global_prenorm(q_out, xc, dev(wl.w_k), dev(wl.block_table), dev(L + 1))
+    torch.cuda.synchronize()
+    ref_o = oracle.paged_decode_global_prenorm(q_bits, expected, wl.w_k, wl.block_table, L + 1, "bf16")
+    err = max_abs(o.cpu().numpy().astype(np.float64), ref_o)
+    print(f"[prenorm append] decode after append: max-abs error {err:.3e}", flush=True)
+    assert err <= BF16_TOL
