@@ -11,17 +11,17 @@
  *
  *   - attn_decode_sliding: slidingDecodeGQA. The query sits at the last
  *     position L-1 of the L = seq_lens[b] cached tokens and sees the keys with
- *     L-1-window < l <= L-1 (slidingGQA's "p - w < l <= p"), i.e. exactly
- *     min(L, window) keys. Separate k and v caches.
+ *     L-1-window < l <= L-1 (the window predicate of slidingGQA with
+ *     p = L-1), i.e. exactly min(L, window) keys. Separate k and v caches.
  *   - attn_decode_global: decodeGQA. Every cached position is visible, and
  *     values equal keys ("values = keys" on the global layers), so one cache
  *     is read as both k and v. Long sequences are split over workgroups and
  *     the per-split results are merged with their log-sum-exp values inside
  *     the call.
  *
- *   The softmax scale is fixed at 1 (the q/k norms take its place on this
- *   model), so it is not an argument. A sequence with no visible key
- *   (L = 0, or window = 0) gets an all-zero output row.
+ *   The softmax scale is fixed at 1 (this model normalises q and k per head
+ *   instead of scaling the logits), so it is not an argument. A sequence
+ *   with no visible key (L = 0, or window = 0) gets an all-zero output row.
  *
  * Paged KV layout (page = 16 tokens, the model's page size):
  *   block_table : int32 [batch][max_pages_per_seq], row-major. Entry j of row
@@ -251,7 +251,6 @@ da_status attn_kv_append_global_prenorm(const float* q_raw, const float* x_raw, 
                                         const int32_t* block_table, const int32_t* positions, void* x_cache,
                                         void* q_out, const da_shape* shape, void* stream);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
 /*
  * Several queries per sequence (chunked prefill, speculative verification):
  * causalGQA and slidingGQA of the Op Specs (Attention.lean) with consecutive
@@ -298,6 +297,7 @@ da_status attn_multiquery_global(const void* q, const int32_t* q_start, int32_t 
 da_status attn_multiquery_workspace_bytes(const da_shape* shape, int32_t max_queries, int32_t window,
                                           size_t* bytes);
 
+/* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(da_status status);
 
 #ifdef __cplusplus

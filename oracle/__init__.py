@@ -22,12 +22,24 @@ Sources (the pages are data; every formula here is restated, not pasted):
   ``Rope.lean`` (``invFreq``, ``rope``) and ``Attention.lean``
   (``sigmoidGate``); Op Specs overview, "Scalar functions" (``sigmoid``).
 
-Pins: every function here is checked in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_norm_rope.py`` against something other than itself
-(literal brute force over the Lean predicates, 50-digit mpmath evaluation,
-torch's scaled_dot_product_attention and rms_norm and a rotate-half RoPE from
-transformers as library special cases, complex-number rotation, closed forms
-and invariants). No function is "parity unpinned".
+Pins (each against something other than the oracle itself):
+
+* attention definitions and the paged front end: ``tests/test_oracle_pins.py``,
+  ``tests/test_oracle_paged.py``, ``tests/test_oracle_merge.py`` (literal
+  brute force over the Lean predicates, 50-digit mpmath, torch's
+  scaled_dot_product_attention, closed forms and invariants);
+* norms, RoPE and the gate: ``tests/test_oracle_norm_rope.py`` (torch's
+  rms_norm, transformers' rotate-half RoPE, complex rotation, mpmath, scipy's
+  expit);
+* the decode-step preparation (``decode_step_qkv_sliding``,
+  ``decode_step_qk_global``) and the k / v derivation of
+  ``paged_decode_global_prenorm``: ``tests/test_oracle_decode_step.py``,
+  against torch's rms_norm, a complex rotation with the Model Spec constants
+  typed in the test, and torch attention, with planted mistakes (wrong theta
+  or active count, w_q for k, RoPE before the norm, v through the weighted
+  norm) that must each fail a pin.
+
+No function is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401

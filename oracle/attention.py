@@ -13,11 +13,11 @@ import numpy as np
 
 
 def softmax_visible(s, visible):
-    """``softmax s visible`` (Attention.lean, "Softmax over the reals,
-    normalized only over visible positions").
+    """``softmax s visible`` (Op Specs page of google/gemma-4-12B,
+    Attention.lean, ``softmax``).
 
-    A visible position ``l`` gets exp(s_l) / sum over visible m of exp(s_m);
-    an invisible one gets 0. If nothing is visible every weight is 0 (the Lean
+    The normaliser runs over the visible positions alone: position ``l`` gets
+    exp(s_l) / sum over visible m of exp(s_m) when it is visible, else 0. If nothing is visible every weight is 0 (the Lean
     definition never evaluates the denominator then).
 
     The largest visible logit is subtracted before exponentiating. Numerator
@@ -54,7 +54,8 @@ def _gqa(scale, visible, q, k, v):
 
 
 def causal_gqa(scale, pos, q, k, v):
-    """``causalGQA scale pos q k v``: query s sees keys l with l <= pos[s]."""
+    """``causalGQA scale pos q k v``: key l is visible to query s iff
+    l <= pos[s]."""
     pos = np.asarray(pos, dtype=np.int64)
     L = np.asarray(k).shape[0]
     l = np.arange(L, dtype=np.int64)
@@ -63,8 +64,9 @@ def causal_gqa(scale, pos, q, k, v):
 
 
 def sliding_gqa(scale, window, pos, q, k, v):
-    """``slidingGQA scale window pos q k v``: query at position p sees keys l
-    with l <= p and p < l + window (equivalently p - window < l <= p)."""
+    """``slidingGQA scale window pos q k v``: with p = pos[s], key l is
+    visible to query s iff l <= p and p < l + window, an interval of at most
+    ``window`` keys ending at p."""
     pos = np.asarray(pos, dtype=np.int64)
     L = np.asarray(k).shape[0]
     l = np.arange(L, dtype=np.int64)
@@ -80,9 +82,10 @@ def _last_position(L):
 
 
 def decode_gqa(scale, q, k, v):
-    """``decodeGQA scale q k v``: the causalGQA output of a single query at the
-    last position L - 1 of L cached tokens. q : [Hkv, G, D]; query head c*G+g
-    reads KV head c (the index layout of q already encodes that)."""
+    """``decodeGQA scale q k v``: causalGQA with one query placed at L - 1,
+    the newest of the L cached positions, so that every key is visible.
+    q : [Hkv, G, D]; the KV head of query head c*G+g is c (the index layout
+    of q already encodes that)."""
     L = np.asarray(k).shape[0]
     return causal_gqa(scale, [_last_position(L)], np.asarray(q)[None], k, v)[0]
 
@@ -90,9 +93,9 @@ def decode_gqa(scale, q, k, v):
 def sliding_decode_gqa(scale, window, q, k, v):
     """``slidingDecodeGQA`` (the graph label of the sliding-window decode node).
 
-    The pages give it no Lean definition; the Op Specs NOTE says it is decode
-    attention over the last ``w`` cached positions with the window semantics of
-    ``slidingGQA``. Reading taken: slidingGQA with one query at pos = L - 1, so
+    The pages give it no Lean definition; the note on the Op Specs overview
+    page describes it as one-query attention restricted to the newest ``w``
+    cached positions, windowed as in ``slidingGQA``. Reading taken: slidingGQA with one query at pos = L - 1, so
     the visible keys are L - window < l <= L - 1, i.e. exactly min(L, window)
     keys (none when window = 0).
     """

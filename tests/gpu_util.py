@@ -37,5 +37,14 @@ def tol(kv_dtype):
     return BF16_TOL if kv_dtype == "bf16" else F32_TOL
 
 
+def oracle_rows_parallel(fn, rows, workers=16):
+    """fn(row) -> oracle output of one sequence, for every row, computed in a
+    thread pool (NumPy releases the GIL in its kernels); stacked in order."""
+    import concurrent.futures
+    rows = list(rows)
+    with concurrent.futures.ThreadPoolExecutor(min(workers, max(1, len(rows)))) as ex:
+        return np.stack(list(ex.map(fn, rows)))
+
+
 def max_abs(a, b):
     return float(np.max(np.abs(a - b))) if a.size else 0.0

@@ -1,7 +1,10 @@
-"""Pins of the oracle's global decode from the pre-norm projection
+"""Checks of the oracle's global decode from the pre-norm projection
 (paged_decode_global_prenorm): the cache layout against an independent
-scatter, closed forms, an invariance, and the equivalence with the sliding
-decode oracle over separately built k and v caches."""
+scatter, a closed form, an invariance, and its consistency with the sliding
+decode oracle over separately built k and v caches. The k / v derivation
+itself is pinned against independent references (torch's rms_norm, a
+complex rotation with the Model Spec constants, torch attention) in
+test_oracle_decode_step.py."""
 
 import numpy as np
 import pytest
@@ -37,9 +40,11 @@ def test_single_key_is_its_unit_norm_row():
 
 
 def test_equals_sliding_decode_over_separate_caches():
-    # Build row-major k and v caches from the same x (k: weighted norm then
-    # RoPE at the token's position, v: unit norm) and run the sliding decode
-    # oracle with a window covering every key (full causal decode).
+    # Consistency, not a pin of the k derivation: build row-major k and v
+    # caches from the same x (k: weighted norm then RoPE at the token's
+    # position, v: unit norm) and run the sliding decode oracle with a window
+    # covering every key (full causal decode); the paged gather, the page
+    # walk and the attention of the two oracle paths must agree.
     seq_lens = [3, 40, 17]
     wl = I.make_global_prenorm(seq_lens, kv_dtype="bf16", tag=(3,), poison=False)
     got = oracle.paged_decode_global_prenorm(wl.q, wl.x_cache, wl.w_k, wl.block_table, wl.seq_lens, "bf16")
@@ -66,22 +71,3 @@ def test_invariant_to_the_scale_of_x():
     b = oracle.paged_decode_global_prenorm(wl.q, wl.x_cache * np.float32(8), wl.w_k, wl.block_table,
                                            wl.seq_lens, "f32")
     np.testing.assert_allclose(b, a * 1.0, atol=1e-3)  # only eps breaks the invariance
-
-
-def test_planted_mistakes_fail():
-    seq_lens = [25]
-    wl = I.make_global_prenorm(seq_lens, kv_dtype="f32", tag=(5,), poison=False)
-    good = oracle.paged_decode_global_prenorm(wl.q, wl.x_cache, wl.w_k, wl.block_table, wl.seq_lens, "f32")
-    # the same computation with v through the weighted norm, or with RoPE
-    # at positions shifted by one, must differ visibly
-    x = P.gather_prenorm_cache(wl.x_cache, wl.block_table[0], np.arange(25)).astype(np.float64)
-    pos = np.arange(25)[:, None]
-    k = oracle.rope(theta=1e6, rot=512, denom=512, active=64, pos=pos, x=oracle.rmsnorm(1e-6, x, wl.w_k))
-    k_shift = oracle.rope(theta=1e6, rot=512, denom=512, active=64, pos=pos + 1,
-                          x=oracle.rmsnorm(1e-6, x, wl.w_k))
-    q = wl.q[0].astype(np.float64).reshape(1, 16, 512)
-    v_w = oracle.rmsnorm(1e-6, x, wl.w_k)
-    v = oracle.rmsnorm_unit(1e-6, x)
-    assert np.max(np.abs(oracle.decode_gqa(1.0, q, k, v_w).reshape(16, 512) - good[0])) > 1e-2
-    assert np.max(np.abs(oracle.decode_gqa(1.0, q, k_shift, v).reshape(16, 512) - good[0])) > 1e-3
-    np.testing.assert_allclose(oracle.decode_gqa(1.0, q, k, v).reshape(16, 512), good[0], atol=1e-12)
