@@ -139,10 +139,12 @@ def time_cold(fn, n, flush):
     return float(np.median(times))
 
 
-def time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, num_splits):
+def time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, num_splits, oracle_threads, cpu_out):
     """Context for the step's numbers, timed after it: the read bandwidth the
     kernels' access pattern reaches (HBM probe), the calls with cold caches,
-    and the long-context global call (B = 2, lengths 131072 and 262144)."""
+    and the long-context global call (B = 2, lengths 131072 and 262144).
+    With oracle_threads > 0 the oracle is also timed on the long-context
+    layer (both sequences, stored bytes copied back) into cpu_out."""
     import types
     import torch
     from decode_attention_amd import probe as P
@@ -186,6 +188,13 @@ def time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, num_splits):
     res["long_context_GBps"] = round(lb / (l_hot * 1e-6) / 1e9, 1)
     res["long_context_us_cold_median"] = round(l_cold, 2)
     res["long_context_GBps_cold"] = round(lb / (l_cold * 1e-6) / 1e9, 1)
+    if oracle_threads > 0:
+        h = I.sample_to_host(dl, [0, 1])
+        t = time_oracle_rows(oracle_global_fn(h), [0, 1], oracle_threads)
+        cpu_out["long_context_global_bf16_B2"] = {"seconds": round(t, 3), "GBps": round(lb / t / 1e9, 4),
+                                                  "sample": "both sequences (one thread each)"}
+        log(f"oracle: long context {t:.1f} s")
+        del h
     log("context: " + ", ".join(f"{k}={v}" for k, v in res.items() if not k.endswith("workload")))
     del dl, out, buf, flush
     torch.cuda.empty_cache()
@@ -211,47 +220,80 @@ def to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def cpu_baseline(sl, gl, sl_bytes_fn, gl_bytes_fn, budget_s):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np
-    import oracle
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    done_b = 0
-    t_total = 0.0
-    # sliding: sequences in order until a third of the budget is used
-    ns = 0
-    t0 = time.perf_counter()
-    while ns < len(sl.seq_lens) and time.perf_counter() - t0 < budget_s / 3:
-        r = slice(ns, ns + 4)
-        oracle.paged_decode_sliding(sl.q[r], sl.k_cache, sl.v_cache, sl.block_table[r], sl.seq_lens[r],
-                                    sl.window, sl.kv_dtype)
-        ns = min(ns + 4, len(sl.seq_lens))
-    t_sl = time.perf_counter() - t0
-    sub = type(sl)(sl.q[:ns], sl.k_cache, sl.v_cache, sl.block_table[:ns], sl.seq_lens[:ns], sl.window,
-                   sl.kv_dtype, sl.Hkv, sl.G, sl.D)
-    done_b += sum(sl_bytes_fn(sub).values())
-    ng = 0
-    t0 = time.perf_counter()
-    while ng < len(gl.seq_lens) and time.perf_counter() - t0 < 2 * budget_s / 3:
-        r = slice(ng, ng + 1)
-        oracle.paged_decode_global(gl.q[r], gl.kv_cache, gl.block_table[r], gl.seq_lens[r], gl.kv_dtype)
-        ng += 1
-    t_gl = time.perf_counter() - t0
-    sub = type(gl)(gl.q[:ng], gl.kv_cache, gl.block_table[:ng], gl.seq_lens[:ng], gl.kv_dtype,
-                   gl.Hkv, gl.G, gl.D)
-    done_b += sum(gl_bytes_fn(sub).values())
-    t_total = t_sl + t_gl
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_workers():
+    """Threads the oracle baseline runs on: the cores this process may use,
+    at most 16 (a one-GPU machine's share of its host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def time_oracle_rows(fn, rows, workers):
+    """Wall seconds of fn(row) over every row, in a pool of `workers` threads
+    with the BLAS pools pinned to one thread each (NumPy releases the GIL in
+    its kernels, so the sequences run in parallel)."""
+    import concurrent.futures
+    from threadpoolctl import threadpool_limits
+    rows = list(rows)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(min(workers, len(rows))) as ex:
+            list(ex.map(fn, rows))
+        return time.perf_counter() - t0
+
+
+def oracle_sliding_fn(wl):
+    import oracle
+    return lambda b: oracle.paged_decode_sliding(wl.q[b:b + 1], wl.k_cache, wl.v_cache, wl.block_table[b:b + 1],
+                                                 wl.seq_lens[b:b + 1], wl.window, wl.kv_dtype)
+
+
+def oracle_global_fn(wl):
+    import oracle
+    return lambda b: oracle.paged_decode_global(wl.q[b:b + 1], wl.kv_cache, wl.block_table[b:b + 1],
+                                                wl.seq_lens[b:b + 1], wl.kv_dtype)
+
+
+def cpu_baseline(sl, gl, workers):
+    """The oracle as it stands (fp64 NumPy) on the step's own workload, both
+    calls in full (64 + 64 sequences), and on the tiny fp32 sliding case."""
+    from decode_attention_amd import inputs as I
+    t_sl = time_oracle_rows(oracle_sliding_fn(sl), range(len(sl.seq_lens)), workers)
+    t_gl = time_oracle_rows(oracle_global_fn(gl), range(len(gl.seq_lens)), workers)
+    b_sl, b_gl = sum(sliding_bytes(sl).values()), sum(global_bytes(gl).values())
+    tiny = I.config_workload(0)
+    t_tiny = time_oracle_rows(oracle_sliding_fn(tiny), range(len(tiny.seq_lens)), workers)
+    b_tiny = sum(sliding_bytes(tiny).values())
+    log(f"oracle: sliding B=64 {t_sl:.2f} s, global B=64 {t_gl:.2f} s, tiny fp32 {t_tiny:.3f} s "
+        f"on {workers} threads")
     return {
-        "value": round(done_b / t_total / 1e9, 4),
+        "value": round((b_sl + b_gl) / (t_sl + t_gl) / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": int(workers),
         "kind": "oracle",
-        "sample": (f"{ns} of 64 sliding sequences ({t_sl:.1f} s) and {ng} of 64 global sequences "
-                   f"({t_gl:.1f} s) of the same workload, fp64 NumPy, algorithmic bytes / wall time"),
+        "cpu_model": cpu_model(),
+        "sample": (f"the whole step workload: all 64 sliding and all 64 global sequences, one sequence per "
+                   f"task on {workers} threads (one BLAS thread each), fp64 NumPy; algorithmic bytes of "
+                   f"both calls / wall time ({t_sl + t_gl:.1f} s)"),
+        "workloads": {
+            "tiny_sliding_fp32_B4": {"seconds": round(t_tiny, 6), "GBps": round(b_tiny / t_tiny / 1e9, 4),
+                                     "sample": "all 4 sequences"},
+            "sliding_bf16_B64": {"seconds": round(t_sl, 6), "GBps": round(b_sl / t_sl / 1e9, 4),
+                                 "sample": "all 64 sequences"},
+            "global_bf16_B64": {"seconds": round(t_gl, 6), "GBps": round(b_gl / t_gl / 1e9, 4),
+                                "sample": "all 64 sequences"},
+        },
     }
 
 
@@ -333,7 +375,7 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
     return extra
 
 
-def time_sweep(da, I, n_steps):
+def time_sweep(da, I, n_steps, oracle_threads, cpu_out):
     """The full decode step of the model: 48 layer calls (layer i global iff
     i % 6 == 5) at B = 256, lengths log-uniform in [1, 131072], every layer
     with its own caches (drawn on the device). Timed after the B = 64 step,
@@ -359,7 +401,8 @@ def time_sweep(da, I, n_steps):
             da.attn_decode_global(dl.q, *dl.caches, dl.block_table, dl.seq_lens, out=outs["global"])
 
     def wl(dl):
-        return types.SimpleNamespace(seq_lens=dl.host_seq_lens, window=dl.window, kv_dtype="bf16",
+        lens = dl.host_seq_lens if hasattr(dl, "host_seq_lens") else dl.seq_lens
+        return types.SimpleNamespace(seq_lens=lens, window=getattr(dl, "window", 0), kv_dtype="bf16",
                                      Hkv=dl.Hkv, G=dl.G, D=dl.D)
 
     nbytes = {k: 0 for k in ("sliding", "global")}
@@ -400,6 +443,25 @@ def time_sweep(da, I, n_steps):
         "sweep_global_GBps": round(nbytes["global"] / 8 / (np.mean(us["global"]) * 1e-6) / 1e9, 1),
     }
     log("sweep: " + ", ".join(f"{k}={v}" for k, v in res.items() if k != "sweep_workload"))
+    if oracle_threads > 0:
+        # the oracle on a seeded sample of 4 sequences through all 48 layers
+        # (stored bytes copied back), extrapolated to the whole step by bytes
+        rows = np.sort(np.random.default_rng(4).choice(len(sl), 4, replace=False))
+        t_s, b_s = 0.0, 0
+        for dl in layers:
+            h = I.sample_to_host(dl, rows)
+            fn = oracle_sliding_fn(h) if dl.kind == "sliding" else oracle_global_fn(h)
+            t_s += time_oracle_rows(fn, range(len(rows)), oracle_threads)
+            b_s += sum((sliding_bytes if dl.kind == "sliding" else global_bytes)(wl(h)).values())
+            del h
+        rate = b_s / t_s
+        cpu_out["full_step_48_calls_B256"] = {
+            "seconds_sampled": round(t_s, 3), "GBps": round(rate / 1e9, 4),
+            "seconds_per_step_extrapolated": round(total / rate, 1),
+            "sample": (f"sampled: sequences {rows.tolist()} of 256 (lengths "
+                       f"{sl[rows].tolist()}) through all 48 layers, 4 threads; rate extrapolated to the "
+                       f"whole step by algorithmic bytes")}
+        log(f"oracle: sweep sample {t_s:.1f} s, {rate / 1e9:.3f} GB/s")
     del layers, outs
     torch.cuda.empty_cache()
     return res
@@ -410,7 +472,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing on the host")
     ap.add_argument("--num-splits", type=int, default=0, help="global kernel workgroups (0 = auto)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, copy this many MiB device-to-device once, so that a "
@@ -533,19 +595,23 @@ def main():
         log(f"copied {args.copy_calibration_mib} MiB device-to-device for counter calibration")
         del src, dst
 
+    threads = oracle_workers() if not args.no_cpu_baseline else 0
+    cpu_more = {}
     extra = {} if args.no_extras else time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb,
                                                   max(args.steps, 10), args.num_splits)
     if not args.no_extras:
-        extra.update(time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, args.num_splits))
+        extra.update(time_context(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, args.num_splits,
+                                  threads, cpu_more))
     if not (args.no_extras or args.no_sweep):
-        extra.update(time_sweep(da, I, 5))
+        extra.update(time_sweep(da, I, 5, threads, cpu_more))
 
     current = counters_current() and args.num_splits == 0  # counters taken at the default split
     traffic = GLOBAL_TRAFFIC["bytes_per_call"] if current else None
     cpu = None
-    if args.cpu_budget > 0:
-        log(f"timing the oracle on a bounded sample (~{args.cpu_budget:.0f} s)")
-        cpu = cpu_baseline(sl, gl, sliding_bytes, global_bytes, args.cpu_budget)
+    if threads > 0:
+        log(f"timing the oracle on the step's workload ({threads} threads)")
+        cpu = cpu_baseline(sl, gl, threads)
+        cpu["workloads"].update(cpu_more)
 
     res = {
         "metric": METRIC,
@@ -593,6 +659,12 @@ def main():
             "unit": "GB/s",
             "frac": round(g_ach / HBM_PEAK_GBS, 4),
             "traffic": traffic,
+            "timing": ("event-timed: HIP events on the library's stream around each attn_decode_global call "
+                       "of K steps (both kernels of the call, plus the dispatch gap after the preceding "
+                       "sliding call); algorithmic bytes of the call / mean event time"),
+            "traffic_source": (None if traffic is None else
+                               "FETCH_SIZE x2 + WRITE_SIZE x1 per call from rocprofv3 --pmc passes, "
+                               "profiles/decode_attn_B64_seqU1-32768_hbm_counters.md"),
         },
         "cpu_baseline": cpu,
     }

@@ -33,6 +33,45 @@ def test_header_declares_the_expected_api():
     assert declared_functions() == sorted(B.EXPORTS)
 
 
+def declared_prototypes():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for m in re.finditer(r"^\s*((?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\([^;]*\))\s*;", text, flags=re.M):
+        protos[m.group(2)] = re.sub(r"\s+", " ", m.group(1)).replace("( ", "(").replace(" )", ")")
+    return protos
+
+
+# The hot path's four calls, as this library declares them. Two departures
+# from the plain boundary sketch are deliberate (the workspace size comes
+# back through a pointer so that the call can report an invalid shape, and
+# the split knob counts workgroups over the batch's page list).
+PATH_PROTOTYPES = {
+    "attn_decode_sliding": "da_status attn_decode_sliding(const void* q, const void* k_cache, const void* v_cache,"
+                           " const int32_t* block_table, const int32_t* seq_lens, int32_t window, void* out,"
+                           " const da_shape* shape, void* stream)",
+    "attn_decode_global": "da_status attn_decode_global(const void* q, const void* kv_cache,"
+                          " const int32_t* block_table, const int32_t* seq_lens, void* out,"
+                          " const da_shape* shape, void* workspace, size_t workspace_bytes, void* stream)",
+    "attn_decode_global_workspace_bytes": "da_status attn_decode_global_workspace_bytes(const da_shape* shape,"
+                                          " size_t* bytes)",
+    "attn_status_string": "const char* attn_status_string(da_status status)",
+}
+
+
+def test_hot_path_signatures():
+    protos = declared_prototypes()
+    for name, want in PATH_PROTOTYPES.items():
+        assert protos[name] == want, name
+
+
+def test_shape_struct_matches_the_binding():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct da_shape \{(.*?)\} da_shape;", text, flags=re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+)\s*;", body)
+    assert fields == [f for f, _ in B.DaShape._fields_]
+    assert len(re.findall(r";", body)) == len(fields)  # every member is an int32_t
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name

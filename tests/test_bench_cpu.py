@@ -75,3 +75,20 @@ def test_benchmark_workloads_are_the_seeded_ones():
     g = bench.global_bytes(_wl(gl, kv_dtype="bf16", Hkv=1, G=16, D=512))
     assert sum(g.values()) == 1144870420
     assert int(((gl.astype(np.int64) + 15) // 16).sum()) == 69701  # pages of the global call
+
+
+def test_cpu_baseline_describes_its_run():
+    # Small stand-ins for the step's two workloads: the baseline times every
+    # sequence of both, on the threads it reports, and names the CPU.
+    sl = I.make_sliding([1, 17, 1030, 40], kv_dtype="bf16", tag=(31,), **I.SLIDING)
+    gl = I.make_global([5, 300, 17], kv_dtype="bf16", tag=(32,), **I.GLOBAL)
+    res = bench.cpu_baseline(sl, gl, 3)
+    assert res["kind"] == "oracle" and res["unit"] == "GB/s" and res["value"] > 0
+    assert res["cores"] == 3 and "3 threads" in res["sample"]
+    assert isinstance(res["cpu_model"], str) and res["cpu_model"]
+    w = res["workloads"]
+    assert set(w) == {"tiny_sliding_fp32_B4", "sliding_bf16_B64", "global_bf16_B64"}
+    b = sum(bench.sliding_bytes(sl).values()) + sum(bench.global_bytes(gl).values())
+    t = w["sliding_bf16_B64"]["seconds"] + w["global_bf16_B64"]["seconds"]
+    assert abs(res["value"] - b / t / 1e9) <= 1e-2 * res["value"] + 1e-4
+    assert 1 <= bench.oracle_workers() <= 16
