@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     attn_decode_sliding,
     attn_decode_global,
     attn_decode_global_workspace_bytes,
+    attn_decode_global_noalloc,
     attn_decode_sliding_gated,
     attn_decode_global_gated,
     attn_decode_global_prenorm,

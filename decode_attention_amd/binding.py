@@ -44,6 +44,7 @@ class DaShape(ctypes.Structure):
 
 
 EXPORTS = ("attn_decode_sliding", "attn_decode_global", "attn_decode_global_workspace_bytes",
+           "attn_decode_global_noalloc",
            "attn_decode_sliding_gated", "attn_decode_global_gated", "attn_decode_global_prenorm",
            "attn_kv_append_sliding", "attn_kv_append_global", "attn_kv_append_global_prenorm",
            "attn_multiquery_sliding", "attn_multiquery_global", "attn_multiquery_workspace_bytes",
@@ -72,6 +73,8 @@ def load_library():
         lib.attn_decode_global.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp,
                                            ctypes.c_size_t, vp]
         lib.attn_decode_global.restype = ctypes.c_int32
+        lib.attn_decode_global_noalloc.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp]
+        lib.attn_decode_global_noalloc.restype = ctypes.c_int32
         lib.attn_decode_sliding_gated.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int32, vp, vp,
                                                   ctypes.POINTER(DaShape), vp]
         lib.attn_decode_sliding_gated.restype = ctypes.c_int32
@@ -229,6 +232,23 @@ def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=N
     given, one is allocated and cached per device, stream and size (calls on
     one stream run in order, so they may share it)."""
     return _global(q, kv_cache, block_table, seq_lens, None, out, workspace, num_splits, stream)
+
+
+def attn_decode_global_noalloc(q, kv_cache, block_table, seq_lens, out, num_splits=0, stream=None):
+    """attn_decode_global on the library's own device scratch array: the
+    library call allocates nothing, and neither does this wrapper (out is
+    required). Calls that may overlap on one device race."""
+    import torch
+    lib = load_library()
+    _check_common(q, block_table, seq_lens, (kv_cache,))
+    shape = _global_shape(q, kv_cache, block_table, num_splits)
+    B, Hq, D = q.shape
+    _require(out is not None and out.dtype == torch.float32 and out.is_contiguous()
+             and tuple(out.shape) == (B, Hq, D) and out.device == q.device,
+             "out must be contiguous fp32 [B, Hq, D] on q's device")
+    _check(lib.attn_decode_global_noalloc(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+                                          _ptr(out), ctypes.byref(shape), _stream(stream)))
+    return out
 
 
 def attn_decode_global_gated(q, kv_cache, block_table, seq_lens, gate, out=None, workspace=None, num_splits=0,

@@ -199,6 +199,28 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                        stream);
 }
 
+da_status attn_decode_global_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, void* out, const da_shape* shape, void* stream) {
+  da_status st = check_global_shape(shape);
+  if (st != DA_OK) return st;
+  if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  st = current_device(&dev, &cus);
+  if (st != DA_OK) return st;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  int max_splits = 0;
+  st = da::global_scratch(dev, &scratch, &scratch_bytes, &max_splits);
+  if (st != DA_OK) return st;
+  // the default split (one workgroup per compute unit) is capped at what the
+  // scratch array holds; an explicit split beyond it is refused
+  const int splits = shape->num_splits > 0 ? shape->num_splits : (cus < max_splits ? cus : max_splits);
+  if (splits > max_splits) return DA_ERR_WORKSPACE;
+  if (da::global_workspace_bytes(*shape, splits) > scratch_bytes) return DA_ERR_WORKSPACE;
+  return da::launch_global(q, kv_cache, block_table, seq_lens, nullptr, nullptr, out, *shape, splits, scratch,
+                           (hipStream_t)stream);
+}
+
 da_status attn_decode_global_prenorm(const void* q, const void* x_cache, const float* w_k,
                                      const int32_t* block_table, const int32_t* seq_lens, void* out,
                                      const da_shape* shape, void* workspace, size_t workspace_bytes, void* stream) {

@@ -55,6 +55,8 @@
 // half B % 2, k-step B / 2, so a rotation pair (d, d + 256), d < 64, sits in
 // one lane: k-steps 0 and 4 of each half. Angles: pos * theta^(-d/256) in
 // revolutions, in fp64, wrapped to [-1/2, 1/2] before the fp32 sin/cos.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -746,6 +748,36 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
     }
     *reinterpret_cast<f32x4*>(ob) = o;
   }
+}
+
+// Device memory of the allocation-free global call: the header and the
+// partial slots of at most kGScratchSplits workgroups (16.9 MB). Every device
+// the library runs on holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device array: its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is passed to kernels.
+constexpr int kGScratchSplits = 256;
+constexpr size_t kGScratchBytes = kGHeaderBytes + (size_t)2 * kGScratchSplits * kGSlotFloats * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kGScratchBytes];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kScratchMaxDevices];
+}  // namespace
+
+da_status global_scratch(int dev, void** ptr, size_t* bytes, int* max_splits) {
+  if (dev < 0 || dev >= kScratchMaxDevices) return DA_ERR_NO_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {  // first call on this device (it is current)
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return DA_ERR_LAUNCH;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  *bytes = kGScratchBytes;
+  *max_splits = kGScratchSplits;
+  return DA_OK;
 }
 
 int global_num_splits(const da_shape& s, int num_cus) {

@@ -19,6 +19,11 @@ da_status launch_sliding(const void* q, const void* k_cache, const void* v_cache
 int global_num_splits(const da_shape& s, int num_cus);
 size_t global_workspace_bytes(const da_shape& s, int num_splits);
 
+// Device address (on device `dev`, which must be current) and size of the
+// library's own scratch array for the allocation-free global call, and the
+// largest split it holds.
+da_status global_scratch(int dev, void** ptr, size_t* bytes, int* max_splits);
+
 // w_k: null for the K=V cache; the k-norm weight [512] for the pre-norm cache.
 da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
                         const int32_t* seq_lens, const float* gate, const float* w_k, void* out,

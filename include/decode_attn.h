@@ -144,6 +144,27 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_decode_global without a caller-provided workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The partial results live in a
+ * scratch array the library holds in device memory (16.9 MB per device, for
+ * at most 256 workgroups); the call allocates nothing.
+ *   Arguments, shapes and results as for attn_decode_global. num_splits = 0
+ *   uses one workgroup per compute unit, at most 256; an explicit num_splits
+ *   above 256 returns DA_ERR_WORKSPACE.
+ *   Every call on a device uses that device's one scratch array: calls that
+ *   may overlap on one device (different streams without ordering) race and
+ *   give undefined results. Calls ordered on a stream are safe; nothing in
+ *   the array needs clearing between calls.
+ * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_WORKSPACE,
+ * DA_ERR_NO_DEVICE or DA_ERR_LAUNCH (also when the scratch array's device
+ * address cannot be resolved).
+ */
+da_status attn_decode_global_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                     const int32_t* seq_lens, void* out, const da_shape* shape,
+                                     void* stream);
+
+/*
  * Global decode from the shared pre-norm projection (pages: gemma-4-12b Model
  * Spec, compute-graph nodes attn.qk_norm, attn.v_norm, attn.rope of the
  * global layers; Op Specs Norm.lean rmsnorm / rmsnormUnit and Rope.lean rope).

@@ -138,6 +138,23 @@ def test_global_validation(lib):
     assert glob(lib, _gshape(batch=5000)) == -2
 
 
+def glob_noalloc(lib, shape, ptrs=None):
+    p = ptrs or [FAKE] * 5
+    return lib.attn_decode_global_noalloc(p[0], p[1], p[2], p[3], p[4], ctypes.byref(shape), NULL)
+
+
+def test_global_noalloc_validation(lib):
+    assert glob_noalloc(lib, _gshape(batch=-1)) == -1
+    assert glob_noalloc(lib, _gshape(), ptrs=[FAKE, FAKE, FAKE, FAKE, NULL]) == -1
+    assert glob_noalloc(lib, _gshape(group=8)) == -2
+    assert glob_noalloc(lib, _gshape(batch=5000)) == -2
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_global_noalloc_no_device_after_valid_arguments(lib):
+    assert glob_noalloc(lib, _gshape()) == -4
+
+
 def test_workspace_bytes_with_explicit_splits(lib):
     assert da.attn_decode_global_workspace_bytes(_gshape(num_splits=1)) == 0
     n = da.attn_decode_global_workspace_bytes(_gshape(num_splits=10))
