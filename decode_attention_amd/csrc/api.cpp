@@ -7,6 +7,7 @@
 #include <cstring>
 #include <mutex>
 
+#include "../../include/decode_attn_trace.h"
 #include "launch.hpp"
 
 namespace {
@@ -86,7 +87,8 @@ da_status decode_sliding(const void* q, const void* k_cache, const void* v_cache
 
 da_status decode_global(const void* q, const void* kv_cache, const int32_t* block_table, const int32_t* seq_lens,
                         const float* gate, void* out, const da_shape* shape, void* workspace,
-                        size_t workspace_bytes, void* stream, const float* w_k = nullptr) {
+                        size_t workspace_bytes, void* stream, const float* w_k = nullptr,
+                        unsigned long long* trace = nullptr) {
   da_status st = check_global_shape(shape);
   if (st != DA_OK) return st;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
@@ -97,7 +99,7 @@ da_status decode_global(const void* q, const void* kv_cache, const int32_t* bloc
   const size_t need = da::global_workspace_bytes(*shape, splits);
   if (need > 0 && (!workspace || workspace_bytes < need)) return DA_ERR_WORKSPACE;
   return da::launch_global(q, kv_cache, block_table, seq_lens, gate, w_k, out, *shape, splits, workspace,
-                           (hipStream_t)stream);
+                           (hipStream_t)stream, trace);
 }
 
 constexpr int kMaxQueries = 1 << 18;  // the model's position domain
@@ -197,6 +199,14 @@ da_status attn_decode_global(const void* q, const void* kv_cache, const int32_t*
                              void* workspace, size_t workspace_bytes, void* stream) {
   return decode_global(q, kv_cache, block_table, seq_lens, nullptr, out, shape, workspace, workspace_bytes,
                        stream);
+}
+
+da_status attn_decode_global_traced(const void* q, const void* kv_cache, const int32_t* block_table,
+                                    const int32_t* seq_lens, void* out, const da_shape* shape, void* workspace,
+                                    size_t workspace_bytes, uint64_t* trace, void* stream) {
+  if (!trace) return DA_ERR_INVALID_ARG;
+  return decode_global(q, kv_cache, block_table, seq_lens, nullptr, out, shape, workspace, workspace_bytes, stream,
+                       nullptr, reinterpret_cast<unsigned long long*>(trace));
 }
 
 da_status attn_decode_global_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,

@@ -100,6 +100,7 @@ struct GlobalArgs {
   const float* gate;         // [B][16][512] sigmoidGate epilogue, or null
   int* ws_hdr;               // [B+1] page prefix, then [B] clamped lengths
   float* ws;                 // [2*G][kGSlotFloats] partial slots
+  unsigned long long* trace; // [G][4] per-workgroup timeline (TRACE instance only)
   int B, P_max, G;
 };
 
@@ -168,6 +169,10 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// s_getreg operands: hwreg(HW_REG_XCC_ID, 0, 16) and hwreg(HW_REG_HW_ID, 0, 32)
+constexpr int kHwRegXccId = 20 | (15 << 11);
+constexpr int kHwRegHwId = 4 | (31 << 11);
+
 constexpr double kPreTheta = 1000000.0;  // RoPE base of the global layers
 constexpr int kPreActive = 64;           // active frequencies (pairs d, d + 256 with d < 64)
 constexpr float kPreEps = 1e-6f;
@@ -193,7 +198,9 @@ __device__ __forceinline__ int tile_coord(int hf, int t) {
   return PRE ? 64 * (t >> 1) + 32 * hf + 16 * (t & 1) : kGSlice * hf + 16 * t;
 }
 
-template <bool PRE>
+// TRACE: the instance behind attn_decode_global_traced, which also writes a
+// per-workgroup timeline entry; the production instances carry none of it.
+template <bool PRE, bool TRACE = false>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) void global_decode_kernel(GlobalArgs a) {
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
@@ -220,6 +227,13 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     }
   }
 
+  // timeline of this workgroup (start time, segments flushed), kept in LDS so
+  // that no register stays live across the page walk for it
+  __shared__ unsigned long long s_trace[TRACE ? 2 : 1];
+  if (TRACE && threadIdx.x == 0) {
+    s_trace[0] = __builtin_amdgcn_s_memrealtime();
+    s_trace[1] = 0;
+  }
   build_prefix(a, s_pre, s_len, s_tmp);
   const int N = rfl(s_pre[a.B]);
   const int w = blockIdx.x;
@@ -376,6 +390,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     __syncthreads();  // the merge area is page space again
     reset_state();
     seg_active = false;
+    if (TRACE && threadIdx.x == 0) ++s_trace[1];
   };
 
   if (R0 < R1) {
@@ -632,6 +647,15 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     wait_vmem_all();
     if (seg_active) flush();
   }
+  if (TRACE && threadIdx.x == 0) {
+    // timeline entry: start and end (100 MHz real-time counter), XCC id and
+    // segments, pages and the hardware id of the first wave
+    unsigned long long* t = a.trace + 4 * (size_t)w;
+    t[0] = s_trace[0];
+    t[1] = __builtin_amdgcn_s_memrealtime();
+    t[2] = (unsigned long long)(__builtin_amdgcn_s_getreg(kHwRegXccId) & 0xF) | (s_trace[1] << 8);
+    t[3] = (unsigned long long)(unsigned)(R1 - R0) | ((unsigned long long)__builtin_amdgcn_s_getreg(kHwRegHwId) << 32);
+  }
 }
 
 // Log-sum-exp merge of the partial results of split sequences. Workgroup:
@@ -793,8 +817,10 @@ size_t global_workspace_bytes(const da_shape& s, int num_splits) {
 
 da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
                         const int32_t* seq_lens, const float* gate, const float* w_k, void* out,
-                        const da_shape& s, int num_splits, void* workspace, hipStream_t stream) {
+                        const da_shape& s, int num_splits, void* workspace, hipStream_t stream,
+                        unsigned long long* trace) {
   GlobalArgs a;
+  a.trace = trace;
   a.w_k = w_k;
   a.q = (const uint16_t*)q;
   a.kv = (const uint16_t*)kv_cache;
@@ -812,6 +838,9 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   a.G = num_splits;
   if (w_k)
     hipLaunchKernelGGL(global_decode_kernel<true>, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
+  else if (trace)
+    hipLaunchKernelGGL((global_decode_kernel<false, true>), dim3((unsigned)num_splits), dim3(kGThreads), 0, stream,
+                       a);
   else
     hipLaunchKernelGGL(global_decode_kernel<false>, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;

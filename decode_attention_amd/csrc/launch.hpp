@@ -25,9 +25,11 @@ size_t global_workspace_bytes(const da_shape& s, int num_splits);
 da_status global_scratch(int dev, void** ptr, size_t* bytes, int* max_splits);
 
 // w_k: null for the K=V cache; the k-norm weight [512] for the pre-norm cache.
+// trace: null, or [num_splits][4] uint64 per-workgroup timeline entries.
 da_status launch_global(const void* q, const void* kv_cache, const int32_t* block_table,
                         const int32_t* seq_lens, const float* gate, const float* w_k, void* out,
-                        const da_shape& s, int num_splits, void* workspace, hipStream_t stream);
+                        const da_shape& s, int num_splits, void* workspace, hipStream_t stream,
+                        unsigned long long* trace = nullptr);
 
 // Decode-step norm + RoPE of the new tokens and their append to the caches.
 da_status launch_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw, const float* w_q,

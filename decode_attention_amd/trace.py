@@ -1,0 +1,149 @@
+"""Per-workgroup timeline of the global decode call (measurement support, not
+part of the attention path): ``attn_decode_global_traced`` from
+include/decode_attn_trace.h runs the global call's kernels and has every
+workgroup of the decode kernel record its start and end time, its XCC and
+its page count.
+
+``python -m decode_attention_amd.trace`` prints a summary for the global
+layer workload (B = 64, lengths uniform in [1, 32768]) and the long-context
+one (B = 2, lengths 131072 and 262144): when the workgroups start, how their
+end times spread, per XCC, next to the call's time by HIP events.
+"""
+
+import ctypes
+import sys
+
+import numpy as np
+
+from .binding import (_check, _check_common, _global_shape, _ptr, _stream, attn_decode_global_workspace_bytes,
+                      load_library)
+
+TICK_US = 0.01  # the real-time counter runs at 100 MHz
+
+
+def _lib():
+    lib = load_library()
+    if not getattr(lib, "_trace_ready", False):
+        vp = ctypes.c_void_p
+        from .binding import DaShape
+        lib.attn_decode_global_traced.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(DaShape), vp, ctypes.c_size_t,
+                                                  vp, vp]
+        lib.attn_decode_global_traced.restype = ctypes.c_int32
+        lib._trace_ready = True
+    return lib
+
+
+def global_timeline(q, kv_cache, block_table, seq_lens, out, num_splits=0, stream=None):
+    """Runs the global call once with the timeline; returns (out, entries)
+    with entries int64 [splits, 4] as the header describes them."""
+    import torch
+    lib = _lib()
+    _check_common(q, block_table, seq_lens, (kv_cache,))
+    shape = _global_shape(q, kv_cache, block_table, num_splits)
+    need = attn_decode_global_workspace_bytes(shape)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    splits = num_splits if num_splits > 0 else torch.cuda.get_device_properties(q.device).multi_processor_count
+    tr = torch.zeros((splits, 4), dtype=torch.int64, device=q.device)
+    _check(lib.attn_decode_global_traced(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+                                         ctypes.byref(shape), _ptr(ws), need, _ptr(tr), _stream(stream)))
+    torch.cuda.synchronize()
+    return out, tr.cpu().numpy()
+
+
+def summarize(entries):
+    """Start and end times (µs from the first start), per-XCC means."""
+    t0 = entries[:, 0].min()
+    start = (entries[:, 0] - t0) * TICK_US
+    end = (entries[:, 1] - t0) * TICK_US
+    xcc = entries[:, 2] & 0xF
+    segs = entries[:, 2] >> 8
+    pages = entries[:, 3] & 0xFFFFFFFF
+    res = {
+        "workgroups": int(len(entries)),
+        "start_max_us": float(start.max()),
+        "end_mean_us": float(end.mean()),
+        "end_p10_us": float(np.percentile(end, 10)),
+        "end_p50_us": float(np.median(end)),
+        "end_p90_us": float(np.percentile(end, 90)),
+        "end_max_us": float(end.max()),
+        "busy_fraction": float((end - start).sum() / (len(end) * end.max())),
+        "pages_per_workgroup": (int(pages.min()), int(pages.max())),
+        "segments_mean": float(segs.mean()),
+        "per_xcc_end_mean_us": {int(x): float(end[xcc == x].mean()) for x in sorted(set(xcc.tolist()))},
+        "per_xcc_end_max_us": {int(x): float(end[xcc == x].max()) for x in sorted(set(xcc.tolist()))},
+    }
+    return res
+
+
+def format_summary(label, res, event_us=None, pages_total=None):
+    lines = [f"{label}: {res['workgroups']} workgroups, {res['pages_per_workgroup'][0]}-"
+             f"{res['pages_per_workgroup'][1]} pages each, {res['segments_mean']:.2f} segments on average"]
+    if event_us is not None:
+        lines.append(f"  call by HIP events (back to back): {event_us:.1f} us")
+    lines.append(f"  last start {res['start_max_us']:.1f} us; end mean {res['end_mean_us']:.1f}, p10 "
+                 f"{res['end_p10_us']:.1f}, p50 {res['end_p50_us']:.1f}, p90 {res['end_p90_us']:.1f}, "
+                 f"max {res['end_max_us']:.1f} us; busy {100 * res['busy_fraction']:.1f}% of workgroups x span")
+    if pages_total:
+        lines.append(f"  decode kernel span {res['end_max_us']:.1f} us = "
+                     f"{pages_total * 16384 / res['end_max_us'] / 1e3:.0f} GB/s of KV; at the mean end "
+                     f"{pages_total * 16384 / res['end_mean_us'] / 1e3:.0f} GB/s")
+    lines.append("  per XCC mean end: " + " ".join(f"{x}:{v:.1f}" for x, v in res["per_xcc_end_mean_us"].items()))
+    lines.append("  per XCC max end:  " + " ".join(f"{x}:{v:.1f}" for x, v in res["per_xcc_end_max_us"].items()))
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    import argparse
+    import torch
+    ap = argparse.ArgumentParser(description="per-workgroup timeline of the global decode call")
+    ap.add_argument("--dump", default=None, help="also save the raw entries of every traced call (.npz)")
+    args_cli = ap.parse_args(argv)
+    raw = {}
+
+    from . import inputs as I
+    from . import binding as B
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    def event_us(fn, n=20):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    gl = I.config_workload(2)
+    args = [dev(x) for x in (gl.q, gl.kv_cache, gl.block_table, gl.seq_lens)]
+    out = torch.empty((64, 16, 512), dtype=torch.float32, device="cuda")
+    pages = int(((gl.seq_lens.astype(np.int64) + 15) // 16).sum())
+    us = event_us(lambda: B.attn_decode_global(*args, out=out))
+    for rep in range(3):
+        _, e = global_timeline(*args, out)
+        raw[f"b64_{rep}"] = e
+        print(format_summary(f"global B=64 U[1,32768], traced call {rep}", summarize(e), us if rep == 0 else None,
+                             pages), flush=True)
+    dl = I.device_layer("global", [131072, 262144], tag=(3,))
+    out2 = torch.empty((2, 16, 512), dtype=torch.float32, device="cuda")
+    largs = [dl.q, dl.caches[0], dl.block_table, dl.seq_lens]
+    us = event_us(lambda: B.attn_decode_global(*largs, out=out2))
+    for rep in range(2):
+        _, e = global_timeline(*largs, out2)
+        raw[f"long_{rep}"] = e
+        print(format_summary(f"global long context B=2 {{131072, 262144}}, traced call {rep}", summarize(e),
+                             us if rep == 0 else None, (131072 + 262144) // 16), flush=True)
+    if args_cli.dump:
+        np.savez(args_cli.dump, **raw)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -72,6 +72,13 @@ def test_shape_struct_matches_the_binding():
     assert len(re.findall(r";", body)) == len(fields)  # every member is an int32_t
 
 
+def test_trace_header_symbol_is_exported(lib):
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "decode_attn_trace.h")).read(), flags=re.S)
+    names = re.findall(r"^\s*\w+\s+(attn_\w+)\s*\(", text, flags=re.M)
+    assert names == ["attn_decode_global_traced"]
+    assert hasattr(lib, "attn_decode_global_traced")
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
