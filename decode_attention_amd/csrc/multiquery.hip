@@ -10,12 +10,13 @@
 //
 // Rows. A query row is one (query, head) pair of one KV head: on sliding
 // layers its G = 2 heads, on global layers the 16 heads of the single KV head.
-// A workgroup takes a block of rows of one (sequence, KV head) with 8 waves of
-// 16 rows x 256 coordinates; with D = 512 two waves share 16 rows, one per
-// coordinate half, and add their partial scores through LDS in a fixed
-// order. Sliding: 128 rows (64 queries) per workgroup; global: 64 rows (4).
+// A workgroup takes a block of 128 rows of one (sequence, KV head): on
+// sliding layers 64 queries (mq_kernel, 8 waves of 16 rows x 256
+// coordinates), on global layers 8 queries (mq_global_kernel, below), so that
+// speculative verification of up to 8 draft tokens reads each sequence's
+// keys once.
 //
-// Keys. The workgroup walks the pages that some row of its block can see,
+// Sliding (mq_kernel). The workgroup walks the pages that some row of its block can see,
 // two pages per step, staged in LDS (double-buffered), with the loads of the
 // next two steps held in registers. Per step and wave:
 //   S^T (16 tokens x 16 rows) = K Q^T: 8 mfma_f32_16x16x32_bf16 per page, K
@@ -39,6 +40,7 @@
 // (unit, piece, pieces, slot). A caller-given number of splits divides every
 // unit into that many pieces instead.
 #include <algorithm>
+#include <utility>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -53,6 +55,15 @@ constexpr int kMTiles = kMSlice / 16;        // 16-coordinate output tiles per w
 constexpr int kMRegion = 16384;              // LDS bytes per region of a step (2 pages of K, or of V)
 constexpr float kMRescale = 32.f;            // lazy-rescale threshold, log2 units
 constexpr int kMPlanThreads = 1024;          // one workgroup lays out a balanced split
+// Pieces per compute unit of a balanced split (measured on the 8-token
+// verification workloads at B = 64). A global workgroup takes all of a
+// compute unit's LDS, so one piece per unit is a single round of workgroups
+// and the fewest partial results to merge.
+#ifndef DA_MQ_PIECES_GLOBAL
+#define DA_MQ_PIECES_GLOBAL 1
+#endif
+constexpr int kMPiecesPerCuSliding = 3;
+constexpr int kMPiecesPerCuGlobal = DA_MQ_PIECES_GLOBAL;
 
 struct MQArgs {
   const uint16_t* q;        // [T][Hq][D] bf16 bits; sequence b's rows from q_start[b]
@@ -75,8 +86,7 @@ template <int D, int G>
 struct MQShape {
   static_assert((D == 256 && G == 2) || (D == 512 && G == 16), "built shapes");
   static constexpr bool kSliding = D == 256;
-  static constexpr int kHalves = D / kMSlice;           // waves per 16-row block
-  static constexpr int kRows = 16 * kMWaves / kHalves;  // rows per workgroup
+  static constexpr int kRows = 128;                     // rows per workgroup
   static constexpr int kQueries = kRows / G;            // queries per workgroup
   static constexpr int kKPage = kSliding ? 8192 : 16384;  // LDS bytes per page of K (and of V)
   static constexpr int kVBase = kSliding ? kMRegion : 0;  // V region (global: V = K)
@@ -152,8 +162,9 @@ __global__ __launch_bounds__(kMPlanThreads) void mq_plan_kernel(MQArgs a) {
 template <int D, int G>
 __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) void mq_kernel(MQArgs a) {
   using C = MQShape<D, G>;
+  static_assert(C::kSliding, "global layers use mq_global_kernel");
+  constexpr int kHalves = 1;  // one wave per 16 rows, all 256 coordinates
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][2 * kMRegion];
-  __shared__ f32x4 s_part[2][kMWaves][kWave];  // partial S^T per page (D = 512)
 
   int blk = blockIdx.x, split = blockIdx.y, bc = blockIdx.z, nsplit = a.nsplit;
   size_t slot_idx = ((size_t)bc * a.nblk + blk) * a.nsplit + split;
@@ -188,7 +199,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wv = mq_rfl(tid / kWave);
-  const int rb = wv / C::kHalves, hf = wv % C::kHalves;
+  const int rb = wv / kHalves, hf = wv % kHalves;
   const int n = lane & 15, g4 = lane >> 4;
   const int r_wg = rb * 16 + n;  // this lane's row within the workgroup
   const int s_r = s0 + r_wg / G;
@@ -297,13 +308,6 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       }
       sp[pg] = x[0] + x[1];
     }
-    if constexpr (C::kHalves == 2) {  // add the two coordinate halves, same order in both waves
-      s_part[0][wv][lane] = sp[0];
-      s_part[1][wv][lane] = sp[1];
-      __syncthreads();
-      sp[0] = s_part[0][wv & ~1][lane] + s_part[0][wv | 1][lane];
-      sp[1] = s_part[1][wv & ~1][lane] + s_part[1][wv | 1][lane];
-    }
     if (!wact) return;
     float sc[8];
 #pragma unroll
@@ -406,6 +410,336 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   }
 }
 
+// ---------------------------------------------------------------- global layers
+// mq_global_kernel: 128 rows (8 queries x 16 heads of the single KV head) per
+// workgroup, in 4 tiles of 32 rows; wave (rt, hf) = (wv / 2, wv % 2) owns row
+// tile rt and coordinates [256 hf, 256 hf + 256). With 32x32 MFMA tiles each
+// K and V element read from LDS serves 32 rows, half the LDS reads per row of
+// 16-row tiles, and a sequence's keys are read once for up to 8 queries.
+//
+// Keys go HBM -> LDS directly (global_load_lds_dwordx4), two pages (32
+// tokens) per step into a ring of 4 steps, loaded three steps ahead (96 KB
+// in flight per workgroup; the ring and the score exchange fill the 160 KB
+// of LDS); within each 1 KB of a page the 16-byte slots are swizzled so that
+// both kinds of reads spread over all banks. A lane whose token no row of
+// the block sees (past the last query's position, or a page past the piece)
+// loads the zero page instead, so the LDS copy holds zeros there whatever
+// the cache holds, NaN included. The waits for these loads are explicit
+// (vmcnt) and the barriers are plain s_barrier (a __syncthreads would also
+// wait for the loads still in flight); the reads of the ring are asm (see
+// qg_read_k2), so the compiler adds no wait for the loads of its own.
+//
+// Per step and wave:
+//   S^T (32 tokens x 32 rows) partial over the wave's 256 coordinates: 16 x
+//     mfma_f32_32x32x16_bf16, K (A operand: lane l = token l % 32,
+//     coordinates 256 hf + 16 i + 8 (l / 32) .. +8 of k-step i) read from
+//     LDS, Q^T held in registers. Each wave adds its partner's partial from
+//     LDS to its own; fp32 addition commutes, so both hold the same sums.
+//   Accumulator element e = 4i + j of lane l holds token 8i + 4(l/32) + j
+//     of row l % 32. The PV product takes P^T straight from it: k-step ks
+//     (16 tokens) uses elements 8 ks .. 8 ks + 7, i.e. k-slot 8h + w is token
+//     16 ks + 8 (w / 4) + 4 h + w % 4 (h = l / 32), and the V^T operand is
+//     read in the same token order with two ds_read_b64_tr_b16 per tile.
+//   O^T (256 coordinates x 32 rows) += V^T P^T: 8 tiles x 2 k-steps of
+//     mfma_f32_32x32x16_bf16, the accumulators in lane order (coordinate
+//     256 hf + 32 t + 8i + 4(l/32) + j of tile t, row l % 32).
+// Registers are the limit (2 waves per SIMD, 256 each: 128 accumulators, 16
+// for S, 64 of query rows), hence the small read batches; a step every row
+// of a tile sees in full skips the mask.
+constexpr int kQGStep = 2 * 16384;   // bytes of keys per step (two pages)
+constexpr int kQGSlice = 256;        // coordinates per wave
+constexpr int kQGDma = kQGStep / kMThreads / 16;  // 16-byte loads per thread and step (4)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// s_waitcnt operands (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; the counters not named are left unconstrained.
+#define DA_WAIT_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
+#define DA_WAIT_LGKM0 0xC07F
+
+__device__ __forceinline__ void qg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t qg_lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+template <int... Is, class F>
+__device__ __forceinline__ void qg_static_for(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+
+// The reads of the key ring are written as asm, each batch with its own
+// lgkmcnt(0): the compiler then adds no wait of its own for the loads into
+// LDS in flight (its analysis of them has given a full vmcnt(0) before the
+// first step of each pass over the ring), and the explicit vmcnt at the top
+// of a step is the only wait for them.
+template <int O0, int O1>
+__device__ __forceinline__ void qg_read_k2(uint32_t a0, uint32_t a1, uint4& r0, uint4& r1) {
+  asm volatile(
+      "ds_read_b128 %0, %2 offset:%4\n\t"
+      "ds_read_b128 %1, %3 offset:%5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1)
+      : "v"(a0), "v"(a1), "i"(O0), "i"(O1));
+}
+template <int O>
+__device__ __forceinline__ void qg_read_v2(uint32_t a0, uint32_t a1, s16x4& r0, s16x4& r1, s16x4& r2, s16x4& r3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "i"(O), "i"(O + 1024));
+}
+
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) void mq_global_kernel(MQArgs a) {
+  using C = MQShape<512, 16>;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k0[kQGStep];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k1[kQGStep];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k2[kQGStep];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k3[kQGStep];
+  __shared__ f32x4 s_x[kMWaves][4][kWave];  // each wave's partial S^T, 4 pieces of 4 elements
+
+  int blk = blockIdx.x, split = blockIdx.y, bc = blockIdx.z, nsplit = a.nsplit;
+  size_t slot_idx = ((size_t)bc * a.nblk + blk) * a.nsplit + split;
+  if (a.balanced) {
+    const int4 dsc = a.desc[blockIdx.x];
+    const int u = mq_rfl(dsc.x);
+    if (u < 0) return;  // no piece for this workgroup
+    blk = u % a.nblk;
+    bc = u / a.nblk;
+    split = mq_rfl(dsc.y);
+    nsplit = mq_rfl(dsc.z);
+    slot_idx = (size_t)mq_rfl(dsc.w);
+  }
+  const int b = bc;  // one KV head
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
+  const int q0 = a.q_start[b];
+  const int S = a.q_start[b + 1] - q0;
+  const int s0 = blk * C::kQueries;
+  if (s0 >= S) return;  // no rows in this block (the merge skips it too)
+  const int s1 = min(S, s0 + C::kQueries) - 1;
+  const int khi = L - S + s1;  // position of the block's last query: the last key any row sees
+  const int np = khi >= 0 ? khi / kPage + 1 : 0;
+  const int ja = (int)((long long)split * np / nsplit);
+  const int jb = (int)((long long)(split + 1) * np / nsplit);
+  const int nsteps = (jb - ja + 1) / 2;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = mq_rfl(tid / kWave);
+  const int rt = wv >> 1, hf = wv & 1;
+  const int n = lane & 31, h = lane >> 5;
+  const int r_wg = 32 * rt + n;   // this lane's row (column of its tiles)
+  const int s_r = s0 + (r_wg >> 4);
+  const int head = r_wg & 15;
+  const bool valid = s_r <= s1;
+  const int pos_r = valid ? L - S + s_r : -1;  // -1: sees nothing
+  const bool wact = s0 + 2 * rt <= s1;        // a tile holds 2 queries: its first one exists
+
+  // Q^T (B operand) for k-step i: row n, coordinates 256 hf + 16 i + 8 h .. +8
+  uint4 qv[16];
+  {
+    const uint16_t* qp = a.q + ((size_t)(q0 + s_r) * 16 + head) * 512 + hf * kQGSlice + 8 * h;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qv[i] = valid ? ld16(qp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Loads of step k: wave w fills bytes [4w, 4w + 4) KB of the step's LDS
+  // region, i.e. page w / 4 of the step's two, 1 KB (four chunks of 16
+  // tokens) per load. Within each 1 KB the 16-byte slots are swizzled: slot p
+  // of chunk c holds token p ^ 4 (c % 4), so that the transposing V reads
+  // (two chunks x four tokens per 16 lanes) and the K reads (16 tokens of a
+  // chunk per 16 lanes) both spread over all LDS banks. Lane l of load u thus
+  // fetches chunk 16 (w % 4) + 4 u + l / 16, token (l % 16) ^ 4 (l / 16). The
+  // wave's page id is loaded one step before its pages.
+  const int pg_w = wv >> 2;
+  const int tok_w = (lane & 15) ^ (4 * (lane >> 4));
+  const int lane_src = ((wv & 3) * 16 + (lane >> 4)) * 128 + tok_w * 8;  // elements, + 512 u
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_page);
+  auto load_id = [&](int k) __attribute__((always_inline)) -> int {
+    // wave-uniform: a scalar load, counted by lgkmcnt, so that vmcnt counts
+    // only the loads into LDS
+    const int j = min(ja + 2 * k + pg_w, max(jb - 1, 0));
+    // (the block table is read-only during the call: the constant address
+    // space lets the compiler use s_load)
+    const __attribute__((address_space(4))) int* bt = (const __attribute__((address_space(4))) int*)a.bt;
+    return bt[(size_t)b * a.P_max + j];
+  };
+  auto issue = [&](int k, int id, uint8_t* buf) __attribute__((always_inline)) {
+    const int j = ja + 2 * k + pg_w;
+    const bool keep = j < jb && j * kPage + tok_w <= khi;
+    const uint16_t* src = (keep ? a.k + (size_t)mq_rfl(id) * (kPage * 512) : zero) + lane_src;
+    uint8_t* dst = buf + wv * (kQGDma * 1024);
+#pragma unroll
+    for (int u = 0; u < kQGDma; ++u)
+      __builtin_amdgcn_global_load_lds(src + 512 * u, (__attribute__((address_space(3))) void*)(dst + u * 1024),
+                                       16, 0, 0);
+  };
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // K reads (A operand): token n (page n / 16), chunk C = 32 hf + 2 i + h of
+  // k-step i, whose chunk index mod 4 is h + 2 (i % 2): two base offsets.
+  const int k_base = (n >> 4) * 16384 + (32 * hf + h) * 256;
+  const int k_off0 = k_base + (((n & 15) ^ (4 * h)) * 16);      // + 512 i, i even
+  const int k_off1 = k_base + (((n & 15) ^ (4 * h + 8)) * 16);  // + 512 i, i odd
+  // V^T reads: lane group g16 = lane / 16, position i16 = lane % 16 supplies
+  // token T = 4 (g16 / 2) + i16 / 4 (+ 8 for the second read, + 16 ks: page
+  // ks), coordinates 256 hf + 32 t + 16 (g16 % 2) + 4 (i16 % 4) .. +4, from
+  // chunk C = 32 hf + 4 t + 2 (g16 % 2) + (i16 % 4) / 2; its slot is
+  // T ^ 4 (C % 4), and the second read's token T + 8 flips bit 3 of it.
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int cl = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+  const int tr_off0 = (32 * hf + cl) * 256 + (((4 * (g16 >> 1) + (i16 >> 2)) ^ (4 * cl)) * 16) +
+                      (i16 & 1) * 8;  // + 16384 ks + 1024 t
+  const int tr_off1 = tr_off0 ^ 128;
+  // The row tile's first row has the smallest position: a step every row of
+  // the tile sees in full needs no mask.
+  const int pos_tile = L - S + s0 + 2 * rt;
+
+  auto compute = [&](int k, const uint8_t* kb) __attribute__((always_inline)) {
+    f32x16 x = {};
+    const uint32_t kb_addr = qg_lds_addr(kb);
+    if (wact) {
+      const uint32_t ka0 = kb_addr + k_off0, ka1 = kb_addr + k_off1;
+      qg_static_for(std::make_integer_sequence<int, 8>{}, [&](auto bi) __attribute__((always_inline)) {
+        constexpr int I = 2 * decltype(bi)::value;
+        uint4 kv0, kv1;
+        qg_read_k2<I * 512, (I + 1) * 512>(ka0, ka1, kv0, kv1);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv0), __builtin_bit_cast(bf16x8, qv[I]),
+                                                    x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv1),
+                                                    __builtin_bit_cast(bf16x8, qv[I + 1]), x, 0, 0, 0);
+      });
+    }
+    // the two coordinate halves of the row tile: half 0's partial plus half 1's
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) s_x[wv][c4][lane] = f32x4{x[4 * c4], x[4 * c4 + 1], x[4 * c4 + 2], x[4 * c4 + 3]};
+    __builtin_amdgcn_s_waitcnt(DA_WAIT_LGKM0);
+    qg_barrier();
+    if (!wact) return;
+    // own partial plus the partner's: the same sum in both waves (fp32
+    // addition commutes)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const f32x4 sx = s_x[wv ^ 1][c4][lane];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) x[4 * c4 + jj] += sx[jj];
+    }
+    const int j0 = ja + 2 * k;
+    if (!(j0 + 2 <= jb && (j0 + 2) * kPage - 1 <= pos_tile)) {
+      // element e = 4 c4 + jj holds token 8 c4 + 4 h + jj of the step (page of that / 16)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
+        const int pos = (j0 + (tok >> 4)) * kPage + (tok & 15);
+        if (!(j0 + (tok >> 4) < jb && pos <= pos_r)) x[e] = -INFINITY;
+      }
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lmax = fmaxf(lmax, x[e]);
+    lmax *= kLog2e;  // log2 units, as m_run
+    // lazy rescaling (as in the decode kernels): the reference m_run moves
+    // only when a score exceeds it by more than kMRescale
+    if (__any(lmax > m_run + kMRescale)) {
+      const float mp = fmaxf(lmax, xor32(lmax));  // the row's max: lanes l and l ^ 32 hold its tokens
+      const float m_new = (mp > m_run + kMRescale) ? mp : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);  // 0 from -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    }
+    // m_run is -inf only while every score so far, this step's included, is -inf
+    const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+    bf16x8 pp[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pp[e >> 3][e & 7] = (__bf16)exp2_fast(__builtin_fmaf(x[e], kLog2e, mneg));  // 0 from -inf
+    // the denominator sums the weights as rounded for the PV product
+    const uint4 p0 = __builtin_bit_cast(uint4, pp[0]), p1 = __builtin_bit_cast(uint4, pp[1]);
+    constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+    l_run = dot2_bf16(p0.x, kOnes, dot2_bf16(p0.y, kOnes, dot2_bf16(p0.z, kOnes, dot2_bf16(p0.w, kOnes, l_run))));
+    l_run = dot2_bf16(p1.x, kOnes, dot2_bf16(p1.y, kOnes, dot2_bf16(p1.z, kOnes, dot2_bf16(p1.w, kOnes, l_run))));
+    const uint32_t va0 = kb_addr + tr_off0, va1 = kb_addr + tr_off1;
+    qg_static_for(std::make_integer_sequence<int, 8>{}, [&](auto bi) __attribute__((always_inline)) {
+      constexpr int ks = decltype(bi)::value >> 2, t0 = 2 * (decltype(bi)::value & 3);
+      s16x4 a0, a1, b0, b1;  // tiles t0 and t0 + 1, first and second read
+      qg_read_v2<ks * 16384 + t0 * 1024>(va0, va1, a0, a1, b0, b1);
+      acc[t0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7)), pp[ks], acc[t0], 0, 0, 0);
+      acc[t0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7)), pp[ks], acc[t0 + 1], 0,
+          0, 0);
+    });
+  };
+
+  // One step. The pages of step k have landed once at most the pages of
+  // steps k + 1 and k + 2 (2 kQGDma loads) are in flight; past the barrier
+  // every wave's part of step k is in LDS and every wave is done with step
+  // k - 1, whose slot then takes step k + 3. The page ids come one step
+  // ahead through scalar loads.
+  int id_n = 0;  // id of step k + 3
+  auto step = [&](int k, const uint8_t* cur, uint8_t* nxt3) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(2 * kQGDma));
+    qg_barrier();
+    issue(k + 3, id_n, nxt3);
+    id_n = load_id(k + 4);
+    compute(k, cur);
+  };
+  if (nsteps > 0) {
+    const int id0 = load_id(0), id1 = load_id(1), id2 = load_id(2);
+    id_n = load_id(3);
+    issue(0, id0, s_k0);
+    issue(1, id1, s_k1);
+    issue(2, id2, s_k2);
+    for (int k = 0; k < nsteps; k += 4) {
+      step(k, s_k0, s_k3);
+      if (k + 1 >= nsteps) break;
+      step(k + 1, s_k1, s_k0);
+      if (k + 2 >= nsteps) break;
+      step(k + 2, s_k2, s_k1);
+      if (k + 3 >= nsteps) break;
+      step(k + 3, s_k3, s_k2);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(0));  // no load into LDS outlives the workgroup
+
+  const float lt = l_run + xor32(l_run);  // the row's denominator (both lanes of the row)
+  // coordinates 256 hf + 32 t + 8 i + 4 h .. +4 of row r_wg: elements 4i .. 4i + 3 of tile t
+  if (nsplit == 1) {
+    if (valid) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;  // nothing visible: 0
+      float* op = a.out + ((size_t)(q0 + s_r) * 16 + head) * 512 + hf * kQGSlice + 4 * h;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(op + 32 * t + 8 * i) =
+              f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]} * inv;
+    }
+  } else {
+    float* slot = a.ws + slot_idx * C::kSlotFloats;
+    float* ap = slot + (size_t)r_wg * 512 + hf * kQGSlice + 4 * h;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(ap + 32 * t + 8 * i) =
+            f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]};
+    if (h == 0 && hf == 0) {
+      slot[C::kRows * 512 + r_wg] = m_run;
+      slot[C::kRows * 512 + C::kRows + r_wg] = lt;
+    }
+  }
+}
+
 // Combines the nsplit partial slots of one row block. Thread item = (row, 4
 // coordinates), one item per thread: the block's items are spread over
 // kMergeChunks workgroups. The pieces are folded with a running max, 4 at a
@@ -476,13 +810,12 @@ mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_
   p.nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
   const long long units = (long long)s.batch * s.num_kv_heads * p.nblk;
   const size_t slot = (sliding ? MQShape<256, 2>::kSlotFloats : MQShape<512, 16>::kSlotFloats) * sizeof(float);
-  // One workgroup runs on a compute unit at a time (8 waves of ~190 VGPRs).
-  // With fewer than two units per compute unit the keys are split, into
-  // three pieces' worth per compute unit: the dispatcher hands the later
-  // pieces to the compute units that finish first (measured on the
-  // verification workloads: 3 and 4 per compute unit best, 1, 2 and 6
-  // slower).
-  const long long target = 3LL * num_cus;
+  // One workgroup runs on a compute unit at a time (8 waves of ~190-250
+  // VGPRs; the global kernel's 128 KB of LDS). With fewer than two units per
+  // compute unit the keys are split, into kMPiecesPerCu pieces' worth per
+  // compute unit: the dispatcher hands the later pieces to the compute units
+  // that finish first, and every piece writes one partial slot.
+  const long long target = (long long)(sliding ? kMPiecesPerCuSliding : kMPiecesPerCuGlobal) * num_cus;
   if (s.num_splits == 0 && units < 2LL * num_cus) {
     // pieces per unit follow its page count, laid out on the device
     p.balanced = 1;
@@ -545,7 +878,7 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
   if (sliding)
     hipLaunchKernelGGL((mq_kernel<256, 2>), grid, dim3(kMThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((mq_kernel<512, 16>), grid, dim3(kMThreads), 0, stream, a);
+    hipLaunchKernelGGL(mq_global_kernel, grid, dim3(kMThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   if (!p.balanced && p.nsplit <= 1) return DA_OK;
   constexpr int kChunksSliding = MQShape<256, 2>::kRows * 256 / 4 / 256;
