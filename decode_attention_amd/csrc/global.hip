@@ -186,6 +186,17 @@ __device__ __forceinline__ uint32_t pack_bf16(__bf16 lo, __bf16 hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
 }
 
+// (a, b) rounded to bf16, packed (a in the low half): one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// hi = bf16(a, b), lo = bf16 of the remainders: a ~ hi + lo to about 2^-17
+__device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = cvt_pk_bf16(a, b);
+  lo = cvt_pk_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
+}
+
 // Logical coordinate of element e of k-step i of half hf, lane group g, in
 // the pre-norm layout (block 2i + hf), or in the K=V layout.
 template <bool PRE>
@@ -216,14 +227,28 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   constexpr int kQParts = PRE ? 2 : 1;
   __shared__ uint4 s_q[kGPair][kGKSteps][kQParts][kWave];
   __shared__ double s_g[PRE ? kPreActive : 1];      // theta^(-d/256) / (2 pi): revolutions per position
-  __shared__ float2 s_w[PRE ? kPreActive : 1];      // (w_k[d], w_k[d + 256])
   __shared__ float s_ss[PRE ? 2 : 1][kGWaves][16];  // per-token sums of squares of each wave's half
+  // The rotation by pos * omega_d, pos = 16 j + t, is the rotation by the
+  // page's angle 16 j omega_d after the one by t omega_d. The second, with
+  // w_k folded in, is a table over the 16 token offsets of a page: entry
+  // [t][d] = (w0 c, w1 s, w1 c, w0 s), c = cos(2 pi t g_d), s = sin(..),
+  // (w0, w1) = (w_k[d], w_k[d + 256]); rows padded by 16 bytes so that the
+  // 16 tokens' reads of one d fall in different banks.
+  __shared__ f32x4 s_rt[PRE ? kPage : 1][PRE ? kPreActive + 1 : 1];
+  // cos and sin of the page angle of the wave's 32 frequencies
+  __shared__ float s_base[PRE ? kGWaves : 1][PRE ? 64 : 1];
 
   if constexpr (PRE) {
-    const int i = threadIdx.x;
-    if (i < kPreActive) {
-      s_g[i] = pow(kPreTheta, -(double)i / 256.0) * 0.15915494309189535;  // 1 / (2 pi)
-      s_w[i] = make_float2(a.w_k[i], a.w_k[i + 256]);
+    for (int i = threadIdx.x; i < kPage * kPreActive; i += blockDim.x) {
+      const int t = i / kPreActive, d = i % kPreActive;
+      const double g = pow(kPreTheta, -(double)d / 256.0) * 0.15915494309189535;  // 1 / (2 pi)
+      if (t == 0) s_g[d] = g;
+      double rev = (double)t * g;
+      rev -= rint(rev);
+      double sn, cs;
+      sincos(rev * 6.283185307179586, &sn, &cs);
+      const double w0 = a.w_k[d], w1 = a.w_k[d + 256];
+      s_rt[t][d] = f32x4{(float)(w0 * cs), (float)(w1 * sn), (float)(w1 * cs), (float)(w0 * sn)};
     }
   }
 
@@ -461,45 +486,53 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
                                                               __builtin_bit_cast(bf16x8, qv[i]), s2[i & 1],
                                                               0, 0, 0);
       } else {
-        // sum of squares of this wave's 256 coordinates of token lane & 15
-        float ss = 0.f;
+        // sum of squares of this wave's 256 coordinates of each token: the
+        // diagonal of K K^T, on the MFMA units (a K row's A-operand registers
+        // are also its B-operand layout as a column of K^T); element (t, t)
+        // sits at lane t + 16 (t / 4), element t % 4
+        f32x4 gram = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < kGKSteps; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ss = dot2_bf16(u4_get(buf[bs][i], e), u4_get(buf[bs][i], e), ss);
-        ss += xor16(ss);
-        ss += xor32(ss);
-        if (g == 0) s_ss[xb][wv][lane] = ss;
+          gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, buf[bs][i]),
+                                                         __builtin_bit_cast(bf16x8, buf[bs][i]), gram, 0, 0, 0);
+        if (((lane & 15) >> 2) == g) {
+          const int e = lane & 3;
+          s_ss[xb][wv][lane & 15] = e == 0 ? gram[0] : (e == 1 ? gram[1] : (e == 2 ? gram[2] : gram[3]));
+        }
         // RoPE of the pairs (d, d + 256), d = 32 hf + 8 g + e: elements e of
-        // k-steps 0 and 4, at position 16 j + (lane & 15); rotated k as hi + lo
+        // k-steps 0 and 4, at position 16 j + (lane & 15); rotated k as hi + lo.
+        // The page angle of the wave's 32 frequencies: lane l gives the cos
+        // (l < 32) or sin of frequency 32 hf + l % 32, in revolutions (fp64,
+        // wrapped to [-1/2, 1/2]; v_sin/v_cos take revolutions).
+        {
+          double rev = (double)(j * kPage) * s_g[32 * hf + (lane & 31)];
+          rev -= rint(rev);
+          const float rf = (float)rev;
+          s_base[wv][lane] = lane < 32 ? __builtin_amdgcn_cosf(rf) : __builtin_amdgcn_sinf(rf);
+        }
         uint4 kr[2][2];  // [k-step 0 / 4][hi / lo]
         {
-          const double posd = (double)(j * kPage + (lane & 15));
+          const float* cb = &s_base[wv][8 * g];
+          const float* sb = &s_base[wv][32 + 8 * g];
+          const f32x4* tab = &s_rt[lane & 15][32 * hf + 8 * g];
           uint32_t k0h[4], k0l[4], k4h[4], k4l[4];
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            __bf16 vh0[2], vl0[2], vh4[2], vl4[2];
+            float k0[2], k4[2];
 #pragma unroll
             for (int hb = 0; hb < 2; ++hb) {
-              const int dd = 32 * hf + 8 * g + 2 * e2 + hb;
-              double rev = posd * s_g[dd];
-              rev -= rint(rev);  // wrapped to [-1/2, 1/2] revolutions
-              float sn, cs;
-              __sincosf((float)rev * 6.28318530717958648f, &sn, &cs);
-              const float2 w2 = s_w[dd];
+              const int e = 2 * e2 + hb;
+              const f32x4 r = tab[e];
               const uint32_t u0 = u4_get(buf[bs][0], e2), u4 = u4_get(buf[bs][4], e2);
-              const float xa = w2.x * (hb ? bf16_hi(u0) : bf16_lo(u0));
-              const float xb = w2.y * (hb ? bf16_hi(u4) : bf16_lo(u4));
-              const float k0 = cs * xa - sn * xb, k4 = cs * xb + sn * xa;
-              vh0[hb] = (__bf16)k0;
-              vl0[hb] = (__bf16)(k0 - (float)vh0[hb]);
-              vh4[hb] = (__bf16)k4;
-              vl4[hb] = (__bf16)(k4 - (float)vh4[hb]);
+              const float x0 = hb ? bf16_hi(u0) : bf16_lo(u0);
+              const float x1 = hb ? bf16_hi(u4) : bf16_lo(u4);
+              const float y0 = r.x * x0 - r.y * x1;  // R(t omega) (w (.) x)
+              const float y1 = r.z * x1 + r.w * x0;
+              k0[hb] = cb[e] * y0 - sb[e] * y1;       // then R(16 j omega)
+              k4[hb] = cb[e] * y1 + sb[e] * y0;
             }
-            k0h[e2] = pack_bf16(vh0[0], vh0[1]);
-            k0l[e2] = pack_bf16(vl0[0], vl0[1]);
-            k4h[e2] = pack_bf16(vh4[0], vh4[1]);
-            k4l[e2] = pack_bf16(vl4[0], vl4[1]);
+            split_bf16(k0[0], k0[1], k0h[e2], k0l[e2]);
+            split_bf16(k4[0], k4[1], k4h[e2], k4l[e2]);
           }
           kr[0][0] = make_uint4(k0h[0], k0h[1], k0h[2], k0h[3]);
           kr[0][1] = make_uint4(k0l[0], k0l[1], k0l[2], k0l[3]);
@@ -544,7 +577,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float sst = s_ss[xb][wv & ~1][4 * g + e] + s_ss[xb][wv | 1][4 * g + e];
-          rr[e] = 1.f / sqrtf(sst * (1.f / kGD) + kPreEps);
+          rr[e] = __builtin_amdgcn_rsqf(sst * (1.f / kGD) + kPreEps);
         }
       }
       xb ^= 1;
