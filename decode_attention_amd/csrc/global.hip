@@ -693,20 +693,24 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
 // Log-sum-exp merge of the partial results of split sequences. Workgroup:
 // (sequence b, output tile T = 16 coordinates of all 16 heads, i.e. one
-// lane-order tile of a partial slot); its NG groups of 64 threads fold the
-// sequence's pieces grp, grp+NG, ... with a running max, U pieces' loads in
-// flight at a time, reading 1 KB contiguous per piece, and are then combined
-// the same way. The pieces are found from the page prefix table in the
-// workspace header.
-template <int NG, int U>
-__global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
+// lane-order tile of a partial slot, or with LW = 16 a quarter of it: 4
+// coordinates of the 16 heads, so that a few long sequences still spread
+// over many workgroups); its NG groups of LW threads fold the sequence's
+// pieces grp, grp+NG, ... with a running max, U pieces' loads in flight at a
+// time, and are then combined the same way. The pieces are found from the
+// page prefix table in the workspace header.
+template <int NG, int U, int LW = kWave>
+__global__ __launch_bounds__(LW * NG) void lse_merge_kernel(GlobalArgs a) {
   constexpr int kTiles = kGPair * kGMTiles;   // 32 tiles of 16 coordinates
-  __shared__ f32x4 s_num[NG][kWave];
-  __shared__ float s_m[NG][kWave], s_den[NG][kWave];
-  const int b = blockIdx.x / kTiles;
-  const int T = blockIdx.x - b * kTiles;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int grp = threadIdx.x / kWave;
+  constexpr int kQ = kWave / LW;              // workgroups per tile
+  __shared__ f32x4 s_num[NG][LW];
+  __shared__ float s_m[NG][LW], s_den[NG][LW];
+  const int bt = blockIdx.x / kQ;
+  const int b = bt / kTiles;
+  const int T = bt - b * kTiles;
+  const int ln = threadIdx.x % LW;
+  const int lane = (kQ == 1 ? 0 : (blockIdx.x % kQ) * LW) + ln;  // lane of the slot's tile
+  const int grp = threadIdx.x / LW;
   const int h = lane & 15, g = lane >> 4;
   const int Tt = T % kGMTiles, Th = T / kGMTiles;  // tile, half
   const int d0 = (a.w_k ? 64 * (Tt >> 1) + 32 * Th + 16 * (Tt & 1) : kGSlice * Th + 16 * Tt) + 4 * g;
@@ -782,21 +786,21 @@ __global__ __launch_bounds__(64 * NG) void lse_merge_kernel(GlobalArgs a) {
       m = mn;
     }
   }
-  s_num[grp][lane] = num;
-  s_m[grp][lane] = m;
-  s_den[grp][lane] = den;
+  s_num[grp][ln] = num;
+  s_m[grp][ln] = m;
+  s_den[grp][ln] = den;
   __syncthreads();
   if (grp == 0) {
-    float M = s_m[0][lane];
+    float M = s_m[0][ln];
 #pragma unroll
-    for (int gq = 1; gq < NG; ++gq) M = fmaxf(M, s_m[gq][lane]);
+    for (int gq = 1; gq < NG; ++gq) M = fmaxf(M, s_m[gq][ln]);
     f32x4 n = {0.f, 0.f, 0.f, 0.f};
     float dd = 0.f;
 #pragma unroll
     for (int gq = 0; gq < NG; ++gq) {
-      const float f = (s_m[gq][lane] == -INFINITY) ? 0.f : exp2_fast(s_m[gq][lane] - M);
-      n += f * s_num[gq][lane];
-      dd += f * s_den[gq][lane];
+      const float f = (s_m[gq][ln] == -INFINITY) ? 0.f : exp2_fast(s_m[gq][ln] - M);
+      n += f * s_num[gq][ln];
+      dd += f * s_den[gq][ln];
     }
     f32x4 o = n * (1.f / dd);
     if (a.gate) {
@@ -884,12 +888,14 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   // loads remain (one for up to 16, 64 and 192 pieces).
   const int est = num_splits / s.batch + 2;
   const unsigned nb = (unsigned)s.batch * (kGPair * kGMTiles);
+  // Beyond 16 pieces (few sequences, so few tiles) a workgroup takes a
+  // quarter tile, four times as many workgroups sharing the reads.
   if (est <= 16)
     hipLaunchKernelGGL((lse_merge_kernel<4, 4>), dim3(nb), dim3(4 * kWave), 0, stream, a);
   else if (est <= 64)
-    hipLaunchKernelGGL((lse_merge_kernel<16, 4>), dim3(nb), dim3(16 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<16, 4, 16>), dim3(4 * nb), dim3(16 * 16), 0, stream, a);
   else
-    hipLaunchKernelGGL((lse_merge_kernel<16, 12>), dim3(nb), dim3(16 * kWave), 0, stream, a);
+    hipLaunchKernelGGL((lse_merge_kernel<16, 12, 16>), dim3(4 * nb), dim3(16 * 16), 0, stream, a);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 
