@@ -143,10 +143,21 @@ def _stream(stream):
 
 
 def make_shape(batch, num_kv_heads, group, head_dim, max_pages_per_seq, num_pages, kv_dtype,
-               num_splits=0):
+               num_splits=0, out_dtype=DA_DTYPE_F32):
     return DaShape(int(batch), int(num_kv_heads), int(group), int(head_dim), PAGE_SIZE,
-                   int(max_pages_per_seq), int(num_pages), int(kv_dtype), DA_DTYPE_F32,
+                   int(max_pages_per_seq), int(num_pages), int(kv_dtype), int(out_dtype),
                    int(num_splits))
+
+
+def _decode_out(out, shape, device):
+    """The decode calls' output: allocated fp32 when not given, else a
+    contiguous fp32 or bf16 tensor of that shape; returns (out, dtype code)."""
+    import torch
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=device)
+    _require(out.dtype in (torch.float32, torch.bfloat16) and out.is_contiguous() and tuple(out.shape) == shape
+             and out.device == device, f"out must be contiguous fp32 or bf16 {list(shape)} on q's device")
+    return out, (DA_DTYPE_BF16 if out.dtype == torch.bfloat16 else DA_DTYPE_F32)
 
 
 def _check_common(q, block_table, seq_lens, caches):
@@ -174,7 +185,8 @@ def _check_gate(gate, out):
 def attn_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out=None, stream=None):
     """slidingDecodeGQA. q [B, Hkv*G, D]; k_cache, v_cache [P, Hkv, 16, D]
     (row-major pages); block_table int32 [B, P_max]; seq_lens int32 [B].
-    Returns out fp32 [B, Hkv*G, D] (allocated if not given)."""
+    Returns out [B, Hkv*G, D]: fp32 (allocated if not given) or the given
+    fp32 or bf16 tensor."""
     return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, None, out, stream)
 
 
@@ -193,11 +205,8 @@ def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stre
     B, Hq, D = q.shape
     P, Hkv, _, Dk = k_cache.shape
     _require(Dk == D and Hq % Hkv == 0, "head shape mismatch")
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D),
-             "out must be contiguous fp32 [B, Hq, D]")
-    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q))
+    out, out_dtype = _decode_out(out, (B, Hq, D), q.device)
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), out_dtype=out_dtype)
     if gate is None:
         _check(lib.attn_decode_sliding(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                        _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),
@@ -210,13 +219,13 @@ def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stre
     return out
 
 
-def _global_shape(q, kv_cache, block_table, num_splits):
+def _global_shape(q, kv_cache, block_table, num_splits, out_dtype=DA_DTYPE_F32):
     B, Hq, D = q.shape
     _require(kv_cache.dim() == 5 and kv_cache.shape[3] == PAGE_SIZE,
              "kv_cache must be tiled [P, Hkv, D/x, 16, x]")
     P, Hkv, nx, _, x = kv_cache.shape
     _require(nx * x == D and Hq % Hkv == 0, "head shape mismatch")
-    return make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), num_splits)
+    return make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), num_splits, out_dtype)
 
 
 def attn_decode_global_workspace_bytes(shape):
@@ -228,7 +237,8 @@ def attn_decode_global_workspace_bytes(shape):
 def attn_decode_global(q, kv_cache, block_table, seq_lens, out=None, workspace=None, num_splits=0,
                        stream=None):
     """decodeGQA with values = keys. q [B, Hkv*G, D]; kv_cache tiled
-    [P, Hkv, D/x, 16, x]; returns out fp32 [B, Hkv*G, D]. When no workspace is
+    [P, Hkv, D/x, 16, x]; returns out [B, Hkv*G, D] (fp32 if allocated here,
+    else the given fp32 or bf16 tensor). When no workspace is
     given, one is allocated and cached per device, stream and size (calls on
     one stream run in order, so they may share it)."""
     return _global(q, kv_cache, block_table, seq_lens, None, out, workspace, num_splits, stream)
@@ -241,11 +251,9 @@ def attn_decode_global_noalloc(q, kv_cache, block_table, seq_lens, out, num_spli
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (kv_cache,))
-    shape = _global_shape(q, kv_cache, block_table, num_splits)
-    B, Hq, D = q.shape
-    _require(out is not None and out.dtype == torch.float32 and out.is_contiguous()
-             and tuple(out.shape) == (B, Hq, D) and out.device == q.device,
-             "out must be contiguous fp32 [B, Hq, D] on q's device")
+    _require(out is not None, "out is required")
+    out, out_dtype = _decode_out(out, tuple(q.shape), q.device)
+    shape = _global_shape(q, kv_cache, block_table, num_splits, out_dtype)
     _check(lib.attn_decode_global_noalloc(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
                                           _ptr(out), ctypes.byref(shape), _stream(stream)))
     return out
@@ -273,12 +281,8 @@ def _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (kv_cache,))
-    shape = _global_shape(q, kv_cache, block_table, num_splits)
-    B, Hq, D = q.shape
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (B, Hq, D),
-             "out must be contiguous fp32 [B, Hq, D]")
+    out, out_dtype = _decode_out(out, tuple(q.shape), q.device)
+    shape = _global_shape(q, kv_cache, block_table, num_splits, out_dtype)
     need = attn_decode_global_workspace_bytes(shape)
     st = _stream(stream)
     if workspace is None and need > 0:

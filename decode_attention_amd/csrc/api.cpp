@@ -56,8 +56,14 @@ da_status check_common(const da_shape* s) {
   if (s->out_dtype != DA_DTYPE_F32 && s->out_dtype != DA_DTYPE_BF16) return DA_ERR_INVALID_ARG;
   if ((long long)s->max_pages_per_seq * s->page_size > (1LL << 30)) return DA_ERR_INVALID_ARG;
   if (s->page_size != da::kPageSizeAbi) return DA_ERR_UNSUPPORTED;
-  if (s->out_dtype != DA_DTYPE_F32) return DA_ERR_UNSUPPORTED;
   return DA_OK;
+}
+
+// The calls whose only output is fp32 (multi-query, appends).
+da_status check_f32_out(const da_shape* s) {
+  da_status st = check_common(s);
+  if (st != DA_OK) return st;
+  return s->out_dtype == DA_DTYPE_F32 ? DA_OK : DA_ERR_UNSUPPORTED;
 }
 
 da_status check_global_shape(const da_shape* s) {
@@ -107,7 +113,7 @@ constexpr int kMaxQueries = 1 << 18;  // the model's position domain
 // Shapes the multi-query kernels are built for: sliding (any Hkv, G 2, D 256)
 // or global (Hkv 1, G 16, D 512), bf16 caches.
 da_status check_multiquery_shape(const da_shape* s, bool sliding, int32_t max_queries) {
-  da_status st = check_common(s);
+  da_status st = check_f32_out(s);
   if (st != DA_OK) return st;
   if (max_queries <= 0) return DA_ERR_INVALID_ARG;
   if (max_queries > kMaxQueries) return DA_ERR_UNSUPPORTED;
@@ -249,7 +255,7 @@ da_status attn_decode_global_gated(const void* q, const void* kv_cache, const in
 da_status attn_kv_append_sliding(const float* q_raw, const float* k_raw, const float* v_raw, const float* w_q,
                                  const float* w_k, const int32_t* block_table, const int32_t* positions,
                                  void* k_cache, void* v_cache, void* q_out, const da_shape* shape, void* stream) {
-  da_status st = check_common(shape);
+  da_status st = check_f32_out(shape);
   if (st != DA_OK) return st;
   if (!q_raw || !k_raw || !v_raw || !w_q || !w_k || !block_table || !positions || !k_cache || !v_cache ||
       !q_out)
@@ -266,7 +272,7 @@ da_status attn_kv_append_sliding(const float* q_raw, const float* k_raw, const f
 da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const float* w_q, const float* w_k,
                                 const int32_t* block_table, const int32_t* positions, void* kv_cache, void* q_out,
                                 const da_shape* shape, void* stream) {
-  da_status st = check_common(shape);
+  da_status st = check_f32_out(shape);
   if (st != DA_OK) return st;
   if (!q_raw || !kv_raw || !w_q || !w_k || !block_table || !positions || !kv_cache || !q_out)
     return DA_ERR_INVALID_ARG;
@@ -282,7 +288,7 @@ da_status attn_kv_append_global(const float* q_raw, const float* kv_raw, const f
 da_status attn_kv_append_global_prenorm(const float* q_raw, const float* x_raw, const float* w_q,
                                         const int32_t* block_table, const int32_t* positions, void* x_cache,
                                         void* q_out, const da_shape* shape, void* stream) {
-  da_status st = check_common(shape);
+  da_status st = check_f32_out(shape);
   if (st != DA_OK) return st;
   if (!q_raw || !x_raw || !w_q || !block_table || !positions || !x_cache || !q_out) return DA_ERR_INVALID_ARG;
   if (shape->head_dim != 512 || shape->kv_dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;

@@ -96,12 +96,13 @@ struct GlobalArgs {
   const uint16_t* kv;        // [P][1][64][16][8] bf16 bits
   const int32_t* bt;         // [B][P_max]
   const int32_t* seq_lens;   // [B]
-  float* out;                // [B][16][512]
+  void* out;                 // [B][16][512], fp32 or (out_bf16) bf16
   const float* gate;         // [B][16][512] sigmoidGate epilogue, or null
   int* ws_hdr;               // [B+1] page prefix, then [B] clamped lengths
   float* ws;                 // [2*G][kGSlotFloats] partial slots
   unsigned long long* trace; // [G][4] per-workgroup timeline (TRACE instance only)
   int B, P_max, G;
+  int out_bf16;              // the output is bf16 (rounded to nearest even), else fp32
 };
 
 // Shared by both kernels: per-sequence page counts and their prefix sums.
@@ -196,6 +197,14 @@ __device__ __forceinline__ void split_bf16(float a, float b, uint32_t& hi, uint3
   hi = cvt_pk_bf16(a, b);
   lo = cvt_pk_bf16(a - bf16_lo(hi), b - bf16_hi(hi));
 }
+// Four consecutive output elements from element e on, in the output's type.
+__device__ __forceinline__ void store_out4(const GlobalArgs& a, size_t e, f32x4 v) {
+  if (a.out_bf16)
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + e) =
+        make_uint2(cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]));
+  else
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + e) = v;
+}
 
 // Logical coordinate of element e of k-step i of half hf, lane group g, in
 // the pre-norm layout (block 2i + hf), or in the K=V layout.
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   }
   if (w == 0 && a.ws_hdr == nullptr) {  // no merge follows: rows of empty sequences are 0 here
     for (int i = threadIdx.x; i < a.B * (kGH * kGD / 4); i += blockDim.x)
-      if (s_len[i / (kGH * kGD / 4)] == 0) reinterpret_cast<f32x4*>(a.out)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s_len[i / (kGH * kGD / 4)] == 0) store_out4(a, (size_t)4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
   }
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -386,18 +395,18 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
       lt += xor32(lt);
       const int pb = rfl(s_pre[seg_b]), pe = rfl(s_pre[seg_b + 1]);
       if (seg_first == pb && seg_end == pe) {  // whole sequence: o[b][h][d]
-        float* dst = a.out + ((size_t)seg_b * kGH + lh) * kGD + 4 * lg;
+        const size_t row = ((size_t)seg_b * kGH + lh) * kGD + 4 * lg;
         const float inv = 1.f / lt;
 #pragma unroll
         for (int t = 0; t < kGMTiles; ++t) {
           f32x4 o = acc[t] * inv;
           const int dt = tile_coord<PRE>(hf, t);
-          if (a.gate) {  // sigmoidGate epilogue (set only when no merge follows)
-            const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + (dst - a.out) + dt);
+          if (a.gate) {  // sigmoidGate epilogue (set when no merge follows, or for bf16 output)
+            const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + row + dt);
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
           }
-          *reinterpret_cast<f32x4*>(dst + dt) = o;
+          store_out4(a, row + dt, o);
         }
       } else {  // partial slot, lane order: 1 KB contiguous per store
         const int slot = 2 * w + (seg_first == R0 ? 0 : 1);
@@ -714,19 +723,20 @@ __global__ __launch_bounds__(LW * NG) void lse_merge_kernel(GlobalArgs a) {
   const int h = lane & 15, g = lane >> 4;
   const int Tt = T % kGMTiles, Th = T / kGMTiles;  // tile, half
   const int d0 = (a.w_k ? 64 * (Tt >> 1) + 32 * Th + 16 * (Tt & 1) : kGSlice * Th + 16 * Tt) + 4 * g;
-  float* ob = a.out + ((size_t)b * kGH + h) * kGD + d0;
+  const size_t ob = ((size_t)b * kGH + h) * kGD + d0;  // output element
   // sigmoidGate epilogue operands, loaded first so that their latency hides
-  // behind the header reads: the gate, and the row as the decode kernel wrote
-  // it (used only if the sequence was not split)
+  // behind the header reads: the gate, and (fp32 output) the row as the
+  // decode kernel wrote it, used only if the sequence was not split (with
+  // bf16 output the decode kernel gates such rows itself)
   f32x4 gt = {0.f, 0.f, 0.f, 0.f}, o1 = gt;
   if (a.gate && grp == 0) {
-    gt = *reinterpret_cast<const f32x4*>(a.gate + (ob - a.out));
-    o1 = *reinterpret_cast<const f32x4*>(ob);
+    gt = *reinterpret_cast<const f32x4*>(a.gate + ob);
+    if (!a.out_bf16) o1 = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.out) + ob);
   }
   const int* pre = a.ws_hdr;
   const int L = pre[a.B + 1 + b];
   if (L == 0) {
-    if (grp == 0) *reinterpret_cast<f32x4*>(ob) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (grp == 0) store_out4(a, ob, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
   const int N = pre[a.B];
@@ -738,10 +748,10 @@ __global__ __launch_bounds__(LW * NG) void lse_merge_kernel(GlobalArgs a) {
   const int w0 = wg_of(pb);
   const int np = wg_of(pe - 1) - w0 + 1;  // pieces
   if (np == 1) {  // finished inside one workgroup: the row is written
-    if (a.gate && grp == 0) {  // in place: the decode kernel left the row ungated
+    if (a.gate && !a.out_bf16 && grp == 0) {  // in place: the decode kernel left the row ungated
 #pragma unroll
       for (int e = 0; e < 4; ++e) o1[e] *= sigmoidf(gt[e]);
-      *reinterpret_cast<f32x4*>(ob) = o1;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + ob) = o1;
     }
     return;
   }
@@ -807,7 +817,7 @@ __global__ __launch_bounds__(LW * NG) void lse_merge_kernel(GlobalArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
     }
-    *reinterpret_cast<f32x4*>(ob) = o;
+    store_out4(a, ob, o);
   }
 }
 
@@ -863,11 +873,13 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   a.kv = (const uint16_t*)kv_cache;
   a.bt = block_table;
   a.seq_lens = seq_lens;
-  a.out = (float*)out;
+  a.out = out;
+  a.out_bf16 = s.out_dtype == DA_DTYPE_BF16 ? 1 : 0;
   // With a merge to follow, the merge applies the gate to every row: a gate
   // load in the decode kernel's flush would wait (in-order vmcnt) for all the
-  // page loads it has in flight.
-  a.gate = num_splits > 1 ? nullptr : gate;
+  // page loads it has in flight. With bf16 output the decode kernel gates
+  // the rows it finishes itself (the merge would round them twice).
+  a.gate = (num_splits > 1 && !a.out_bf16) ? nullptr : gate;
   a.ws_hdr = num_splits > 1 ? (int*)workspace : nullptr;
   a.ws = num_splits > 1 ? (float*)((char*)workspace + kGHeaderBytes) : nullptr;
   a.B = s.batch;

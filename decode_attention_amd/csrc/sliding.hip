@@ -75,7 +75,7 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ seq_lens, int window,
-    const float* __restrict__ gate, float* __restrict__ out, int Hkv, int P_max) {
+    const float* __restrict__ gate, void* __restrict__ out, int out_bf16, int Hkv, int P_max) {
   constexpr int G = 2;
   constexpr int E = Elem<T>::E;
   constexpr int CPR = D / E;
@@ -96,10 +96,17 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
 
   // Lengths beyond the block-table row are clamped so no read leaves it.
   const int L = min(seq_lens[b], P_max * kPage);
-  float* ob = out + ((size_t)b * Hkv * G + (size_t)c * G) * D;
+  // output rows of (b, c), fp32 or (out_bf16) bf16 rounded to nearest even
+  const size_t ob = ((size_t)b * Hkv * G + (size_t)c * G) * D;
+  auto store = [&](int i, float v) __attribute__((always_inline)) {
+    if (out_bf16)
+      reinterpret_cast<__bf16*>(out)[ob + i] = (__bf16)v;
+    else
+      reinterpret_cast<float*>(out)[ob + i] = v;
+  };
   const float* gb = gate ? gate + ((size_t)b * Hkv * G + (size_t)c * G) * D : nullptr;
   if (L <= 0 || window <= 0) {  // no visible key: the output rows are 0
-    for (int i = threadIdx.x; i < G * D; i += NW * kWave) ob[i] = 0.f;
+    for (int i = threadIdx.x; i < G * D; i += NW * kWave) store(i, 0.f);
     return;
   }
   const int lo = L > window ? L - window : 0;  // first visible position
@@ -249,7 +256,7 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
       den = fmaf(f, s_l[w][h], den);
     }
     const float o = num / den;
-    ob[idx] = gb ? o * sigmoidf(gb[idx]) : o;  // sigmoidGate epilogue
+    store(idx, gb ? o * sigmoidf(gb[idx]) : o);  // sigmoidGate epilogue
   }
 }
 
@@ -260,15 +267,16 @@ da_status launch_sliding(const void* q, const void* k_cache, const void* v_cache
                          void* out, const da_shape& s, hipStream_t stream) {
   const dim3 grid((unsigned)s.batch * (unsigned)s.num_kv_heads);
   const dim3 block(kSlidingWaves * kWave);
+  const int out_bf16 = s.out_dtype == DA_DTYPE_BF16 ? 1 : 0;
   if (s.kv_dtype == DA_DTYPE_BF16) {
     hipLaunchKernelGGL((sliding_decode_kernel<uint16_t, 256, kSlidingWaves>), grid, block, 0, stream,
                        (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
-                       block_table, seq_lens, window, gate, (float*)out, s.num_kv_heads,
+                       block_table, seq_lens, window, gate, out, out_bf16, s.num_kv_heads,
                        s.max_pages_per_seq);
   } else {
     hipLaunchKernelGGL((sliding_decode_kernel<float, 256, kSlidingWaves>), grid, block, 0, stream,
                        (const float*)q, (const float*)k_cache, (const float*)v_cache, block_table,
-                       seq_lens, window, gate, (float*)out, s.num_kv_heads, s.max_pages_per_seq);
+                       seq_lens, window, gate, out, out_bf16, s.num_kv_heads, s.max_pages_per_seq);
   }
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }

@@ -93,7 +93,11 @@ typedef struct da_shape {
   int32_t max_pages_per_seq; /* P_max >= 1: length of a block-table row */
   int32_t num_pages;         /* physical pages in the cache pool, >= 1 */
   int32_t kv_dtype;          /* DA_DTYPE_F32 or DA_DTYPE_BF16 (q, k, v) */
-  int32_t out_dtype;         /* DA_DTYPE_F32 */
+  int32_t out_dtype;         /* DA_DTYPE_F32, or DA_DTYPE_BF16 for the decode
+                                calls (sliding, global, gated, pre-norm,
+                                no-alloc): each output element rounded to
+                                nearest even once; the multi-query calls and
+                                the appends take DA_DTYPE_F32 only */
   int32_t num_splits;        /* attn_decode_global: number of workgroups the
                                 cached pages of the whole batch are divided
                                 among (0 = one per compute unit); ignored by
@@ -104,7 +108,7 @@ typedef struct da_shape {
  * slidingDecodeGQA over paged k/v caches (Gemma-4-12B sliding layers:
  * Hkv = 8, G = 2, D = 256, window 1024).
  *   Built shapes: (Hkv, G, D) with G = 2, D = 256, any Hkv >= 1;
- *   kv dtypes fp32 and bf16; out fp32.
+ *   kv dtypes fp32 and bf16; out fp32 or bf16 (shape->out_dtype).
  *   window >= 0 (0 gives zeros). seq_lens: int32 [batch].
  * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_NO_DEVICE or
  * DA_ERR_LAUNCH.
@@ -126,7 +130,8 @@ da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* byte
 /*
  * decodeGQA over a paged K=V cache (Gemma-4-12B global layers: Hkv = 1,
  * G = 16, D = 512, values equal keys).
- *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32;
+ *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32 or bf16
+ *   (shape->out_dtype; the split pieces are merged in fp32 and rounded once);
  *   batch <= 256 (larger batches return DA_ERR_UNSUPPORTED; split them into
  *   calls of at most 256 sequences); num_splits <= 65536.
  *   Work split: the cached pages of the batch are divided into equal,

@@ -121,8 +121,27 @@ def test_sliding_validation(lib):
     s.page_size = 32
     assert sliding(lib, s) == -2
     s = _shape()
+    s.out_dtype = 7
+    assert sliding(lib, s) == -1
+
+
+def test_bf16_output_is_valid_for_the_decode_calls_only(lib):
+    """out_dtype bf16: accepted by the decode calls (which then stop at the
+    device check on a host without a GPU), refused by the multi-query calls
+    and the appends, whose outputs are fp32 only."""
+    s, g = _shape(), _gshape()
     s.out_dtype = B.DA_DTYPE_BF16
-    assert sliding(lib, s) == -2
+    g.out_dtype = B.DA_DTYPE_BF16
+    assert sliding(lib, s) == -4
+    assert sliding_gated(lib, s) == -4
+    assert glob(lib, g) == -4
+    assert global_gated(lib, g) == -4
+    assert glob_noalloc(lib, g) == -4
+    assert mq(lib, s) == -2
+    assert mq(lib, g, sliding=False) == -2
+    assert append_sliding(lib, s) == -2
+    assert append_global(lib, g) == -2
+    assert append_prenorm(lib, g) == -2
 
 
 def _gshape(**kw):
