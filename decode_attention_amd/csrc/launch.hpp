@@ -46,12 +46,13 @@ da_status launch_append_global_prenorm(const float* q_raw, const float* x_raw, c
 
 // Several queries per sequence at its last positions (row f2).
 // Work layout: a fixed number of pieces per unit (sequence, KV head, row
-// block), or (balanced) pieces per unit laid out on the device from the
-// units' page counts over `grid` workgroups.
+// block), or a layout made on the device from the units' page counts over
+// `grid` workgroups: pieces per unit (sliding layers) or equal shares of all
+// units' steps laid end to end (global layers).
 struct mq_plan {
   int nblk;         // row blocks per sequence
   int units;        // batch * num_kv_heads * nblk
-  int balanced;     // 1: layout made on the device
+  int balanced;     // 1: pieces per unit; 2: contiguous shares
   int nsplit;       // fixed split: pieces per unit (1: none)
   int grid;         // balanced: workgroups of the main kernel
   size_t ws_bytes;  // workspace the call needs

@@ -30,15 +30,20 @@
 // rounded values, so every output is a weighted average whose weights are
 // exact to about 2^-9 relative.
 //
-// Split over keys. When sequences x KV heads x row blocks (the units) give
-// too few workgroups for the chip, a unit's pages are divided among several
-// workgroups that write partial (acc, m, l) per row, and mq_merge_kernel
-// combines them: M = max m_i, o = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i.
-// By default the number of pieces of a unit follows its page count, so that
-// long sequences do not form the tail: mq_plan_kernel (one workgroup) lays
-// the pieces out and gives every workgroup of the main kernel a descriptor
-// (unit, piece, pieces, slot). A caller-given number of splits divides every
-// unit into that many pieces instead.
+// Split over keys. A unit (sequence, KV head, row block) may have its pages
+// divided among several workgroups that write partial (acc, m, l) per row,
+// and mq_merge_kernel combines them: M = max m_i,
+// o = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i. By default:
+//   sliding layers, when the units give too few workgroups for the chip: the
+//     number of pieces of a unit follows its page count, so that long
+//     sequences do not form the tail (mq_plan_kernel lays the pieces out and
+//     gives every workgroup a descriptor (unit, piece, pieces, slot));
+//   global layers, always: one workgroup per compute unit, each taking an
+//     equal share of the steps of all units laid end to end
+//     (mq_plan_contig_kernel), so that no workgroup runs longer than the
+//     mean plus one step, whatever the mix of lengths.
+// A caller-given number of splits divides every unit into that many pieces
+// instead.
 #include <algorithm>
 #include <utility>
 
@@ -54,11 +59,11 @@ constexpr int kMKSteps = kMSlice / 32;       // 16x16x32 k-steps per page and wa
 constexpr int kMTiles = kMSlice / 16;        // 16-coordinate output tiles per wave
 constexpr int kMRegion = 16384;              // LDS bytes per region of a step (2 pages of K, or of V)
 constexpr float kMRescale = 32.f;            // lazy-rescale threshold, log2 units
-constexpr int kMPlanThreads = 1024;          // one workgroup lays out a balanced split
-// Pieces per compute unit of a balanced split (measured on the 8-token
+constexpr int kMPlanThreads = 1024;          // one workgroup lays out a split
+// Workgroups per compute unit of a split (measured on the 8-token
 // verification workloads at B = 64). A global workgroup takes all of a
-// compute unit's LDS, so one piece per unit is a single round of workgroups
-// and the fewest partial results to merge.
+// compute unit's LDS, so one per unit is a single round of workgroups and
+// the fewest partial results to merge.
 #ifndef DA_MQ_PIECES_GLOBAL
 #define DA_MQ_PIECES_GLOBAL 1
 #endif
@@ -77,8 +82,11 @@ struct MQArgs {
                             // [grid][slot] (balanced split)
   int* tab;                 // balanced split: [units + 1] first slot of each unit
   int4* desc;               // balanced split: [grid] (unit, piece, pieces, slot); unit -1: no work
+  long long* hdr;           // contiguous split: {steps in all units, steps per workgroup}
+  long long* off;           // contiguous split: [units + 1] first step of each unit
+  int* wfirst;              // contiguous split: [grid] unit holding the workgroup's first step
   int B, Hkv, P_max, window, nblk, nsplit;
-  int balanced;             // 1: pieces per unit follow its page count
+  int balanced;             // 1: pieces per unit follow its page count; 2: contiguous split
   int units, grid;          // balanced split: B*Hkv*nblk units over `grid` workgroups
 };
 
@@ -94,6 +102,14 @@ struct MQShape {
 };
 
 __device__ __forceinline__ int mq_rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Element i of a layout array the plan kernel wrote, read as wave-uniform
+// through the constant address space (a scalar load; the array is not
+// written during the kernel).
+template <typename T>
+__device__ __forceinline__ T mq_sload(const T* p, long long i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
 
 // Pages the rows of unit u = (sequence, KV head, row block) see, as the main
 // kernel walks them (0 for a block without rows).
@@ -157,6 +173,85 @@ __global__ __launch_bounds__(kMPlanThreads) void mq_plan_kernel(MQArgs a) {
   if (tid == kMPlanThreads - 1) a.tab[U] = run;  // the last thread's run is the total
   const int used = (int)s_sum[kMPlanThreads - 1];
   for (int w = used + tid; w < a.grid; w += kMPlanThreads) a.desc[w] = make_int4(-1, 0, 1, 0);
+}
+
+// Exclusive prefix sum over the plan workgroup (kMPlanThreads threads);
+// `total` gets the sum of every thread's value.
+template <typename T>
+__device__ T mq_block_exscan(T v, T* s_w, T& total) {
+  const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+  T inc = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const T y = __shfl_up(inc, d, kWave);
+    if (lane >= d) inc += y;
+  }
+  if (lane == kWave - 1) s_w[wv] = inc;
+  __syncthreads();
+  T before = 0, all = 0;
+  for (int i = 0; i < kMPlanThreads / kWave; ++i) {
+    const T t = s_w[i];
+    if (i < wv) before += t;
+    all += t;
+  }
+  __syncthreads();
+  total = all;
+  return before + inc - v;
+}
+
+// Contiguous split layout (one workgroup), for the global layers. The steps
+// (page pairs) of all units are laid end to end, unit after unit, and
+// workgroup w of the main kernel runs steps [w per, (w + 1) per) of that list,
+// per = ceil(steps / grid): every workgroup gets the same number of steps
+// (one more at most), whatever the units' lengths, at the cost of a
+// workgroup's range crossing unit boundaries. A unit that lies within one
+// workgroup's range is finished by it (its rows written directly); a unit
+// cut by a range boundary is run in pieces, one per workgroup it meets,
+// which write partial slots tab[u] .. tab[u+1]-1 for the merge. Writes
+// hdr = {steps, per}, off[u] (first step of unit u; off[units] = steps),
+// tab, and wfirst[w] (the unit holding workgroup w's first step; -1: w has
+// no steps).
+__global__ __launch_bounds__(kMPlanThreads) void mq_plan_contig_kernel(MQArgs a) {
+  __shared__ long long s_w[kMPlanThreads / kWave];
+  __shared__ int s_wi[kMPlanThreads / kWave];
+  const int tid = threadIdx.x, U = a.units;
+  const int per_t = (U + kMPlanThreads - 1) / kMPlanThreads;
+  const int u0 = min(U, tid * per_t), u1 = min(U, u0 + per_t);
+  auto unit_steps = [&](int u) -> long long { return (mq_unit_pages<512, 16>(a, u) + 1) / 2; };
+  long long loc = 0;
+  for (int u = u0; u < u1; ++u) loc += unit_steps(u);
+  long long tot;
+  const long long base = mq_block_exscan(loc, s_w, tot);
+  long long run = base;
+  const long long per = tot > 0 ? (tot + a.grid - 1) / a.grid : 1;
+  int cnt = 0;
+  for (int u = u0; u < u1; ++u) {
+    const long long ns = unit_steps(u);
+    a.off[u] = run;
+    if (ns > 0) {
+      const long long wf = run / per, wl = (run + ns - 1) / per;
+      if (wl > wf) cnt += (int)(wl - wf + 1);
+      for (long long w = (run + per - 1) / per; w <= wl; ++w) a.wfirst[w] = u;  // ranges starting in u
+    }
+    run += ns;
+  }
+  if (tid == kMPlanThreads - 1) a.off[U] = run;  // the last thread's run is the total
+  int ctot;
+  int crun = mq_block_exscan(cnt, s_wi, ctot);
+  run = base;
+  for (int u = u0; u < u1; ++u) {
+    const long long ns = unit_steps(u);
+    a.tab[u] = crun;
+    if (ns > 0 && (run + ns - 1) / per > run / per) crun += (int)((run + ns - 1) / per - run / per + 1);
+    run += ns;
+  }
+  if (tid == kMPlanThreads - 1) a.tab[U] = crun;
+  const long long nwg = (tot + per - 1) / per;
+  for (long long w = nwg + tid; w < a.grid; w += kMPlanThreads) a.wfirst[w] = -1;
+  if (tid == 0) {
+    a.hdr[0] = tot;
+    a.hdr[1] = per;
+  }
 }
 
 template <int D, int G>
@@ -502,17 +597,51 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   __shared__ __attribute__((aligned(16))) uint8_t s_k3[kQGStep];
   __shared__ f32x4 s_x[kMWaves][4][kWave];  // each wave's partial S^T, 4 pieces of 4 elements
 
-  int blk = blockIdx.x, split = blockIdx.y, bc = blockIdx.z, nsplit = a.nsplit;
-  size_t slot_idx = ((size_t)bc * a.nblk + blk) * a.nsplit + split;
-  if (a.balanced) {
-    const int4 dsc = a.desc[blockIdx.x];
-    const int u = mq_rfl(dsc.x);
-    if (u < 0) return;  // no piece for this workgroup
+  // The workgroup's pieces. Fixed split: one, (row block, piece, sequence)
+  // = blockIdx. Contiguous split: steps [w per, (w + 1) per) of the units
+  // laid end to end, one piece per unit met (the plan kernel's layout),
+  // every value read here wave-uniform (scalar loads).
+  const bool contig = a.balanced == 2;
+  long long g0 = 0, g1 = 0, per = 1;
+  int u = 0;
+  if (contig) {
+    const long long tot = mq_sload(a.hdr, 0);
+    per = mq_sload(a.hdr, 1);
+    g0 = (long long)blockIdx.x * per;
+    g1 = min(g0 + per, tot);
+    if (g0 >= g1) return;  // no steps for this workgroup
+    u = mq_sload(a.wfirst, blockIdx.x);
+  }
+  for (bool first = true;; first = false) {
+  int blk, bc, ja, jb, slot = -1;
+  long long ls0 = 0, ls1 = 0;
+  if (contig) {
+    if (g0 >= g1) break;
+    long long o0 = mq_sload(a.off, u), o1 = mq_sload(a.off, u + 1);
+    while (o1 <= g0) {  // units without steps
+      ++u;
+      o0 = o1;
+      o1 = mq_sload(a.off, u + 1);
+    }
+    const long long e = min(g1, o1);
+    ls0 = g0 - o0;
+    ls1 = e - o0;
+    const int t0 = mq_sload(a.tab, u);
+    if (mq_sload(a.tab, u + 1) > t0) slot = t0 + (int)((long long)blockIdx.x - o0 / per);
     blk = u % a.nblk;
     bc = u / a.nblk;
-    split = mq_rfl(dsc.y);
-    nsplit = mq_rfl(dsc.z);
-    slot_idx = (size_t)mq_rfl(dsc.w);
+    g0 = e;
+    ++u;
+  } else {
+    if (!first) break;
+    blk = blockIdx.x;
+    bc = blockIdx.z;
+    if (a.nsplit > 1) slot = (bc * a.nblk + blk) * a.nsplit + (int)blockIdx.y;
+  }
+  if (!first) {
+    // the previous piece's last step still reads the ring
+    __builtin_amdgcn_s_waitcnt(DA_WAIT_LGKM0);
+    qg_barrier();
   }
   const int b = bc;  // one KV head
   int L = a.seq_lens[b];
@@ -520,12 +649,17 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const int q0 = a.q_start[b];
   const int S = a.q_start[b + 1] - q0;
   const int s0 = blk * C::kQueries;
-  if (s0 >= S) return;  // no rows in this block (the merge skips it too)
+  if (s0 >= S) continue;  // no rows in this block (the merge skips it too)
   const int s1 = min(S, s0 + C::kQueries) - 1;
   const int khi = L - S + s1;  // position of the block's last query: the last key any row sees
   const int np = khi >= 0 ? khi / kPage + 1 : 0;
-  const int ja = (int)((long long)split * np / nsplit);
-  const int jb = (int)((long long)(split + 1) * np / nsplit);
+  if (contig) {
+    ja = (int)(2 * ls0);
+    jb = (int)min(2 * ls1, (long long)np);
+  } else {
+    ja = (int)((long long)blockIdx.y * np / a.nsplit);
+    jb = (int)((long long)(blockIdx.y + 1) * np / a.nsplit);
+  }
   const int nsteps = (jb - ja + 1) / 2;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
@@ -713,7 +847,7 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 
   const float lt = l_run + xor32(l_run);  // the row's denominator (both lanes of the row)
   // coordinates 256 hf + 32 t + 8 i + 4 h .. +4 of row r_wg: elements 4i .. 4i + 3 of tile t
-  if (nsplit == 1) {
+  if (slot < 0) {
     if (valid) {
       const float inv = lt > 0.f ? 1.f / lt : 0.f;  // nothing visible: 0
       float* op = a.out + ((size_t)(q0 + s_r) * 16 + head) * 512 + hf * kQGSlice + 4 * h;
@@ -725,8 +859,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
               f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]} * inv;
     }
   } else {
-    float* slot = a.ws + slot_idx * C::kSlotFloats;
-    float* ap = slot + (size_t)r_wg * 512 + hf * kQGSlice + 4 * h;
+    float* sp = a.ws + (size_t)slot * C::kSlotFloats;
+    float* ap = sp + (size_t)r_wg * 512 + hf * kQGSlice + 4 * h;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
 #pragma unroll
@@ -734,10 +868,11 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
         *reinterpret_cast<f32x4*>(ap + 32 * t + 8 * i) =
             f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]};
     if (h == 0 && hf == 0) {
-      slot[C::kRows * 512 + r_wg] = m_run;
-      slot[C::kRows * 512 + C::kRows + r_wg] = lt;
+      sp[C::kRows * 512 + r_wg] = m_run;
+      sp[C::kRows * 512 + C::kRows + r_wg] = lt;
     }
   }
+  }  // pieces
 }
 
 // Combines the nsplit partial slots of one row block. Thread item = (row, 4
@@ -761,7 +896,14 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
   const int unit = bc * a.nblk + blk;
   const int first = a.balanced ? a.tab[unit] : unit * a.nsplit;
   const int nsplit = a.balanced ? a.tab[unit + 1] - first : a.nsplit;
-  if (nsplit <= 1) return;  // a single piece wrote its rows itself
+  float* op = a.out + ((size_t)(q0 + s_r) * (a.Hkv * G) + c * G + r % G) * D + d;
+  if (nsplit <= 1) {
+    // a single piece wrote its rows itself; in a contiguous split a unit
+    // without a piece either lay within one workgroup's range or sees no key
+    if (a.balanced == 2 && nsplit == 0 && mq_unit_pages<D, G>(a, unit) == 0)
+      *reinterpret_cast<f32x4*>(op) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
   const float* base = a.ws + (size_t)first * C::kSlotFloats;
   float m = -INFINITY, den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
@@ -793,7 +935,6 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
     }
   }
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  float* op = a.out + ((size_t)(q0 + s_r) * (a.Hkv * G) + c * G + r % G) * D + d;
   *reinterpret_cast<f32x4*>(op) = num * inv;
 }
 
@@ -803,6 +944,22 @@ static int mq_blocks(int max_queries) {
 }
 
 static size_t mq_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte offsets in the workspace of a contiguous split's layout arrays; the
+// partial slots follow (at most 2 grid - 2 of them: a unit cut by k range
+// boundaries has k + 1 pieces, and there are grid - 1 boundaries).
+struct mq_contig_offsets {
+  size_t hdr, wfirst, off, tab, total;
+};
+static mq_contig_offsets mq_contig_layout(int grid, int units) {
+  mq_contig_offsets o;
+  o.hdr = 0;
+  o.wfirst = mq_align(2 * sizeof(long long));
+  o.off = o.wfirst + mq_align((size_t)grid * sizeof(int));
+  o.tab = o.off + mq_align(((size_t)units + 1) * sizeof(long long));
+  o.total = o.tab + mq_align(((size_t)units + 1) * sizeof(int));
+  return o;
+}
 
 mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_cus) {
   const bool sliding = s.head_dim == 256;
@@ -816,6 +973,15 @@ mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_
   // compute unit: the dispatcher hands the later pieces to the compute units
   // that finish first, and every piece writes one partial slot.
   const long long target = (long long)(sliding ? kMPiecesPerCuSliding : kMPiecesPerCuGlobal) * num_cus;
+  if (!sliding && s.num_splits == 0) {
+    // global layers: the contiguous split, whatever the number of units
+    p.balanced = 2;
+    p.nsplit = 0;
+    p.units = (int)units;
+    p.grid = (int)target;
+    p.ws_bytes = mq_contig_layout(p.grid, p.units).total + 2 * (size_t)p.grid * slot;
+    return p;
+  }
   if (s.num_splits == 0 && units < 2LL * num_cus) {
     // pieces per unit follow its page count, laid out on the device
     p.balanced = 1;
@@ -859,9 +1025,23 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
   a.ws = nullptr;
   a.tab = nullptr;
   a.desc = nullptr;
+  a.hdr = nullptr;
+  a.off = nullptr;
+  a.wfirst = nullptr;
   const bool sliding = s.head_dim == 256;
   dim3 grid((unsigned)a.nblk, (unsigned)a.nsplit, (unsigned)(s.batch * s.num_kv_heads));
-  if (p.balanced) {
+  if (p.balanced == 2) {
+    uint8_t* w = (uint8_t*)workspace;
+    const mq_contig_offsets o = mq_contig_layout(p.grid, p.units);
+    a.hdr = (long long*)(w + o.hdr);
+    a.wfirst = (int*)(w + o.wfirst);
+    a.off = (long long*)(w + o.off);
+    a.tab = (int*)(w + o.tab);
+    a.ws = (float*)(w + o.total);
+    grid = dim3((unsigned)p.grid, 1, 1);
+    hipLaunchKernelGGL(mq_plan_contig_kernel, dim3(1), dim3(kMPlanThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
+  } else if (p.balanced) {
     uint8_t* w = (uint8_t*)workspace;
     a.desc = (int4*)w;
     a.tab = (int*)(w + mq_align((size_t)p.grid * sizeof(int4)));

@@ -185,3 +185,25 @@ def test_balanced_split_one_long_sequence(gpu_lib):
         err = max_abs(got[s], oracle_row(mq, b, j))
         print(f"[multiquery] one long sequence: b={b} query {j}: max-abs {err:.3e}", flush=True)
         assert err <= BF16_TOL
+
+
+def test_contiguous_split_short_units(gpu_lib):
+    # The global layers' default split lays the steps of all row blocks end
+    # to end and gives each workgroup an equal share: here most shares hold
+    # many short blocks whole (written directly), blocks cut by a share
+    # boundary go through the merge, and blocks with queries but no cached
+    # key (L = 0) or no queries at all are met by no workgroup.
+    rng = np.random.default_rng(911)
+    lens = rng.integers(0, 90, size=300)
+    counts = np.minimum(rng.integers(0, 13, size=300), np.maximum(lens, 1))
+    counts[5::23] = 0
+    lens[::17] = 0
+    counts[::17] = 3  # queries at positions -3 .. -1: all-zero rows
+    lens[7] = 40000  # one block longer than a share
+    counts[7] = 8
+    mq = I.make_multiquery("global", lens, counts, tag=(911,), **I.GLOBAL)
+    got = check(mq, "contiguous split, short units")
+    for b in range(0, 300, 17):
+        s = int(mq.q_start[b])
+        assert np.all(got[s:s + 3] == 0)
+    assert np.array_equal(got, run(mq))
