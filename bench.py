@@ -268,7 +268,7 @@ def oracle_global_fn(wl):
 def cpu_baseline(sl, gl, workers):
     """The oracle as it stands (fp64 NumPy) on the step's own workload, both
     calls in full (64 + 64 sequences), and on the tiny fp32 sliding case."""
-    from decode_attention_amd import inputs as I
+    from workloads import inputs as I
     t_sl = time_oracle_rows(oracle_sliding_fn(sl), range(len(sl.seq_lens)), workers)
     t_gl = time_oracle_rows(oracle_global_fn(gl), range(len(gl.seq_lens)), workers)
     b_sl, b_gl = sum(sliding_bytes(sl).values()), sum(global_bytes(gl).values())
@@ -495,7 +495,7 @@ def main():
     import torch
 
     import decode_attention_amd as da
-    from decode_attention_amd import inputs as I
+    from workloads import inputs as I
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
 import bench  # noqa: E402
-from decode_attention_amd import inputs as I  # noqa: E402
+from workloads import inputs as I  # noqa: E402
 
 
 def _wl(seq_lens, **kw):

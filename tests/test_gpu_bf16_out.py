@@ -16,7 +16,7 @@ import torch
 
 import decode_attention_amd as da
 import oracle
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 from gpu_util import BF16_TOL, dev
 

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 from gpu_util import BF16_TOL, dev, global_on_gpu, max_abs, oracle_rows_parallel
 

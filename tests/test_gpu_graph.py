@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import decode_attention_amd as da
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 from gpu_util import dev
 

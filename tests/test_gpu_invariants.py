@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 from gpu_util import F32_TOL, global_on_gpu, sliding_on_gpu
 

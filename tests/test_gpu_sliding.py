@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import oracle
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 from gpu_util import dev, max_abs, sliding_on_gpu, tol
 

@@ -1,7 +1,7 @@
 """GPU parity on the full decode-step sweep's shapes: B = 256 sequences with
 lengths log-uniform in [1, 131072], a sliding layer (Hkv 8, G 2, D 256,
 window 1024) and a global layer (Hkv 1, G 16, D 512, K = V), caches drawn on
-the device (decode_attention_amd.inputs.device_layer). The oracle computes
+the device (workloads.inputs.device_layer). The oracle computes
 sampled sequences from their stored bytes, copied back from the device.
 
 Bar: max-abs 2e-2 for bf16 KV (fp32 accumulate, fp32 out).
@@ -13,7 +13,7 @@ import torch
 
 import decode_attention_amd as da
 import oracle
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 from gpu_util import BF16_TOL, max_abs
 

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import decode_attention_amd as da
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 from decode_attention_amd import trace as T
 
 from gpu_util import dev

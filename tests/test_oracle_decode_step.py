@@ -28,7 +28,7 @@ import oracle
 from oracle import append as A
 from oracle import norm_rope as NR
 from oracle import paged as P
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 EPS = 1e-6
 # Model Spec constants, typed here (not read from the oracle)

@@ -7,7 +7,7 @@ import pytest
 import oracle
 from oracle import attention as A
 from oracle import paged as P
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 
 def test_bf16_decoding_closed_form():
@@ -152,7 +152,7 @@ def test_block_table_pages_are_distinct_and_guard_is_poisoned():
 
 
 def test_f64_to_bf16_rounding():
-    from decode_attention_amd import inputs as I
+    from workloads import inputs as I
     import torch
     x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.140625, 1.0 + 2**-8 + 2**-40])
     got = oracle.f64_to_bf16_bits(x)

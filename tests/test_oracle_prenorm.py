@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from oracle import paged as P
-from decode_attention_amd import inputs as I
+from workloads import inputs as I
 
 
 def test_layout_round_trip_and_pair_slots():

@@ -1,7 +1,7 @@
 """Runs one benchmark workload's call a number of times, for an external
 profiler (measurement support, not part of the attention path):
 
-    python -m decode_attention_amd.profile_run WORKLOAD [--iters N]
+    python -m workloads.profile_run WORKLOAD [--iters N]
 
 after one untimed call, N calls back to back on the library's stream, then
 the mean time per call by HIP events. The workloads are the ones the
