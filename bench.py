@@ -358,6 +358,19 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
     mq_res["global_prenorm_GBps"] = round((sum(gb.values()) + 512 * 4) / (pre_us * 1e-6) / 1e9, 1)
     log(f"global prenorm {pre_us:.1f} us")
     del d_pw, o_pw
+    # the global call on an fp32 K=V cache: the workload's bf16 values widened
+    # on the device (tiled [P][1][64][16][8] -> [P][1][128][16][4])
+    P = d_gl[1].shape[0]
+    kv32 = d_gl[1].float().view(P, 1, 64, 16, 2, 4).permute(0, 1, 2, 4, 3, 5).reshape(P, 1, 128, 16, 4).contiguous()
+    q32 = d_gl[0].float()
+    o32 = torch.empty((64, 16, 512), dtype=torch.float32, device="cuda")
+    f32_us = time_calls(lambda: da.attn_decode_global(q32, kv32, *d_gl[2:4], out=o32, num_splits=num_splits),
+                        n_extra)
+    mq_res["global_f32kv_us_per_call"] = round(f32_us, 2)
+    mq_res["global_f32kv_GBps"] = round((2 * (gb["kv"] + gb["q"]) + gb["out"] + gb["table"]) / (f32_us * 1e-6) / 1e9,
+                                        1)
+    log(f"global fp32 KV {f32_us:.1f} us")
+    del kv32, q32, o32
     gate_b = 64 * 16 * 4
     extra = {**mq_res,
         "append_sliding_us_per_call": round(app_sl_us, 2),

@@ -69,8 +69,7 @@ da_status check_f32_out(const da_shape* s) {
 da_status check_global_shape(const da_shape* s) {
   da_status st = check_common(s);
   if (st != DA_OK) return st;
-  if (s->num_kv_heads != 1 || s->group != 16 || s->head_dim != 512 || s->kv_dtype != DA_DTYPE_BF16)
-    return DA_ERR_UNSUPPORTED;
+  if (s->num_kv_heads != 1 || s->group != 16 || s->head_dim != 512) return DA_ERR_UNSUPPORTED;
   if (s->batch > kGlobalMaxBatch || s->num_splits > kGlobalMaxSplits) return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
@@ -98,6 +97,8 @@ da_status decode_global(const void* q, const void* kv_cache, const int32_t* bloc
   da_status st = check_global_shape(shape);
   if (st != DA_OK) return st;
   if (!q || !kv_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
+  // the pre-norm cache and the timeline are built for bf16 only
+  if ((w_k || trace) && shape->kv_dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;
   int dev = 0, cus = 0;
   st = current_device(&dev, &cus);
   if (st != DA_OK) return st;

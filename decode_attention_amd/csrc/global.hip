@@ -700,6 +700,353 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   }
 }
 
+// ---------------------------------------------------------------- fp32 cache
+// decodeGQA over an fp32 K=V cache, tiled [pages][1][128][16][4]: chunk c
+// (coordinates 4c .. 4c+3) of token t at floats (16 c + t) * 4 of the page.
+// Same work split, workspace header, partial slots and merge as the bf16
+// kernel; every product is fp32 (mfma_f32_16x16x4f32, fp32 weights), so the
+// result is the exact softmax average up to fp32 rounding.
+//
+// 8 waves: a step takes up to 2 pages of one sequence, page slot pr = wv / 4,
+// and the 4 waves of a page split its 512 coordinates, quarter qd = wv % 4
+// owning [128 qd, 128 qd + 128): 8 KB of the 32 KB page, 8 lane-linear 1 KB
+// loads. Load i puts chunk 32 qd + 4 i + l / 16 of token l % 16 in lane l.
+//   S^T (16 tokens x 16 heads) partial over the wave's 128 coordinates, in
+//     fp64: 32 x mfma_f64_16x16x4f64 on the fp32 values (exact products and
+//     fp64 sums: at D = 512 the scores reach ~100, where fp32 spacing alone
+//     moves a weight by several 1e-6). A = the loaded K (lane t + 16 j,
+//     element e of load i: coordinate 128 qd + 16 i + 4 j + e, i.e. the k
+//     index j of MFMA (i, e) stands for that coordinate), B = Q^T in the same
+//     coordinate order from LDS. The 4 partials of a page are added through
+//     LDS in a fixed order, in fp64.
+//   The fp64 accumulator holds tokens g + 4e of head l % 16 (g = l / 16):
+//     k-step s of the PV product takes tokens 4s .. 4s+3, token 4s + j in k
+//     slot j, so its B operand P^T is element s of the lane's own weights,
+//     unmoved.
+//   O^T += V^T P^T in fp32: the wave's 8 KB of V go to LDS ([token][128
+//     coordinates], 16-byte columns XOR-swizzled by the token) and come back
+//     16 bytes per lane: token 4s + l / 16, coordinates 4 m .. 4 m + 3 with
+//     m = 16 q + l % 16, the A operands of tiles 4q .. 4q+3 (tile 4q + e, row
+//     r = coordinate 128 qd + 4 (16 q + r) + e). 8 tiles x 4 k-steps of
+//     mfma_f32_16x16x4f32, whose accumulator rows are 4 (l / 16) + i.
+// Steps, descriptors and loads run as in the bf16 kernel (page slices of
+// steps k + 1 and k + 2 in flight).
+constexpr int kFPages = 2;              // pages per step
+constexpr int kFQuads = 4;              // waves per page (coordinate quarters)
+constexpr int kFWaves = kFPages * kFQuads;
+constexpr int kFThreads = kFWaves * kWave;
+constexpr int kFSlice = kGD / kFQuads;  // coordinates per wave (128)
+constexpr int kFLoads = kFSlice / 16;   // 1 KB loads per wave and page (8)
+constexpr int kFTiles = kFSlice / 16;   // 16-coordinate output tiles per wave (8)
+constexpr int kFPageFloats = kPage * kGD;
+constexpr float kFRescale = 8.f;        // lazy-rescale threshold, log2 units
+constexpr double kLog2e64 = 1.4426950408889634074;
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+static_assert(kFThreads == kGThreads, "the prefix table is built by the same block size");
+
+__global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) void global_decode_f32_kernel(
+    GlobalArgs a) {
+  __shared__ int s_pre[kGMaxBatch + 1];
+  __shared__ int s_len[kGMaxBatch];
+  __shared__ int s_tmp[kFThreads];
+  __shared__ f64x4 s_part[2][kFWaves][kWave];  // partial S^T tiles, fp64 (double-buffered)
+  // V of each wave's slice ([16 tokens][128 coordinates]); also the merge
+  // area at the end of a segment
+  __shared__ __attribute__((aligned(16))) float s_v[kFWaves][kPage * kFSlice];
+  __shared__ float s_ml[kFQuads][2][kWave];  // m, l of the wave states being merged
+  // Q^T B operands of the current segment: [quarter][load][lane], lane h + 16j
+  // holding head h, coordinates 128 qd + 16 i + 4 j .. +4
+  __shared__ uint4 s_q[kFQuads][kFLoads][kWave];
+
+  const float* qf = reinterpret_cast<const float*>(a.q);
+  const float* kvf = reinterpret_cast<const float*>(a.kv);
+
+  build_prefix(a, s_pre, s_len, s_tmp);
+  const int N = rfl(s_pre[a.B]);
+  const int w = blockIdx.x;
+  if (w == 0 && a.ws_hdr != nullptr) {  // publish the table for the merge kernel
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[i] = s_pre[i];
+    for (int i = threadIdx.x; i < a.B; i += blockDim.x) a.ws_hdr[a.B + 1 + i] = s_len[i];
+  }
+  if (w == 0 && a.ws_hdr == nullptr) {  // no merge follows: rows of empty sequences are 0 here
+    for (int i = threadIdx.x; i < a.B * (kGH * kGD / 4); i += blockDim.x)
+      if (s_len[i / (kGH * kGD / 4)] == 0) store_out4(a, (size_t)4 * i, f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = rfl(threadIdx.x / kWave);
+  const int pr = wv >> 2;    // page slot of a step
+  const int qd = wv & 3;     // coordinate quarter of this wave
+  const int g = lane >> 4;   // this lane's S^T rows: tokens g + 4e
+  const int tk = lane & 15;  // token of this lane's loads; head of its S^T / O^T column
+
+  uint4 buf[kGBuf][kFLoads];  // ring of this wave's page slices
+  int idv[kGBuf];             // physical page ids, 2 steps before their pages
+  int iduse[kGBuf];           // the page slot has a page in that step (else: zero page)
+  f32x4 acc[kFTiles];         // O^T: head tk, coordinate 128 qd + 4 (16 (t / 4) + 4 g + e) + t % 4
+  float m_run = -INFINITY, l_run = 0.f;
+  const size_t qd_off = (size_t)qd * kFSlice * kPage;  // floats: the quarter's chunks
+  float* vs = s_v[wv];
+  // V staging: load i of lane l goes to row tk, 16-byte column (4 i + g) ^ tk
+  // (the XOR keeps each column group of 16 and spreads a write's 16 lanes of
+  // one column over all banks, as it does the reads' 16 columns of one row)
+  const int vw_row = tk * kFSlice;
+
+  int dP[kGDesc], dN[kGDesc], dB[kGDesc], dS[kGDesc], dJ[kGDesc], dL[kGDesc];
+  const int R0 = range_start(w, N, a.G), R1 = range_start(w + 1, N, a.G);
+  int xb = 0;
+  bool seg_active = false;
+  int seg_b = 0, seg_first = 0, seg_end = 0;
+
+  auto reset_state = [&]() __attribute__((always_inline)) {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int t = 0; t < kFTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  // Stage the query rows of sequence b in s_q (after the last use of the
+  // previous ones). Rare: waits for every outstanding load.
+  auto load_q = [&](int b) __attribute__((always_inline)) {
+    const int tid = opaque(threadIdx.x);
+    uint4 t[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int u = 4 * tid + r;  // quarter, load, lane
+      const int f = u / (kFLoads * kWave), i = (u / kWave) % kFLoads, l = u % kWave;
+      t[r] = ld16(qf + ((size_t)b * kGH + (l & 15)) * kGD + kFSlice * f + 16 * i + 4 * (l >> 4));
+    }
+    wait_vmem_all();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) (&s_q[0][0][0])[4 * tid + r] = t[r];
+    __syncthreads();
+  };
+
+  f32x4* st = reinterpret_cast<f32x4*>(&s_v[0][0]);  // 4 states of [8][64] f32x4
+  auto put_state = [&](int k, int ln) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kFTiles; ++t) st[(k * kFTiles + t) * kWave + ln] = acc[t];
+    s_ml[k][0][ln] = m_run;
+    s_ml[k][1][ln] = l_run;
+  };
+  auto take_state = [&](int k, int ln) __attribute__((always_inline)) {
+    const float m_o = s_ml[k][0][ln], l_o = s_ml[k][1][ln];
+    const float M = fmaxf(m_run, m_o);
+    const float fs = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - M);
+    const float fo = (m_o == -INFINITY) ? 0.f : exp2_fast(m_o - M);
+#pragma unroll
+    for (int t = 0; t < kFTiles; ++t) acc[t] = acc[t] * fs + st[(k * kFTiles + t) * kWave + ln] * fo;
+    l_run = l_run * fs + l_o * fo;
+    m_run = M;
+  };
+  // Merge the 2 page-slot states (1 -> 0) and write the segment: the output
+  // row if it is the whole sequence, else a partial slot (the first segment of
+  // the range in slot 2w, the last in slot 2w + 1), in the bf16 kernel's lane
+  // order: coordinate d = 256 f + 16 T + 4 g' + e of head h at lane h + 16 g',
+  // tile T, half f.
+  auto flush = [&]() __attribute__((always_inline)) {
+    const int ln = opaque(lane), lh = ln & 15, lg = ln >> 4;
+    __syncthreads();  // every wave is done with its V region
+    if (pr == 1) put_state(qd, ln);
+    __syncthreads();
+    if (pr == 0) {
+      take_state(qd, ln);
+      float lt = l_run + xor16(l_run);
+      lt += xor32(lt);
+      const int pb = rfl(s_pre[seg_b]), pe = rfl(s_pre[seg_b + 1]);
+      if (seg_first == pb && seg_end == pe) {  // whole sequence: o[b][h][d]
+        const size_t row = ((size_t)seg_b * kGH + lh) * kGD;
+        const float inv = 1.f / lt;
+#pragma unroll
+        for (int q4 = 0; q4 < kFTiles / 4; ++q4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int d = kFSlice * qd + 64 * q4 + 16 * lg + 4 * i;
+            f32x4 o = f32x4{acc[4 * q4][i], acc[4 * q4 + 1][i], acc[4 * q4 + 2][i], acc[4 * q4 + 3][i]} * inv;
+            if (a.gate) {  // sigmoidGate epilogue (set when no merge follows, or for bf16 output)
+              const f32x4 gt = *reinterpret_cast<const f32x4*>(a.gate + row + d);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] *= sigmoidf(gt[e]);
+            }
+            store_out4(a, row + d, o);
+          }
+      } else {
+        const int slot = 2 * w + (seg_first == R0 ? 0 : 1);
+        float* ws = a.ws + (size_t)slot * kGSlotFloats;
+        if (qd == 0 && lg == 0) {
+          ws[kGH * kGD + lh] = m_run;
+          ws[kGH * kGD + kGH + lh] = lt;
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < kFTiles / 4; ++q4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int T = 8 * (qd & 1) + 4 * q4 + lg;
+            *reinterpret_cast<f32x4*>(ws + ((size_t)((qd >> 1) * kGMTiles + T) * kWave + lh + 16 * i) * 4) =
+                f32x4{acc[4 * q4][i], acc[4 * q4 + 1][i], acc[4 * q4 + 2][i], acc[4 * q4 + 3][i]};
+          }
+      }
+    }
+    wait_vmem_all();
+    __syncthreads();  // the merge area is page space again
+    reset_state();
+    seg_active = false;
+  };
+
+  if (R0 < R1) {
+    const int t_end = R1;
+    int gp = R0, gb = seq_of_page(s_pre, a.B, R0);
+    int gpb = rfl(s_pre[gb]), gpe = rfl(s_pre[gb + 1]), gL = rfl(s_len[gb]);
+    size_t last_idx = 0;
+
+    auto gen = [&](int d) __attribute__((always_inline)) {
+      int n = 0, nw = 0;
+      if (gp < t_end) {
+        while (gpe <= gp) {  // next sequence with pages
+          ++gb;
+          gpb = gpe;
+          gpe = rfl(s_pre[gb + 1]);
+          gL = rfl(s_len[gb]);
+        }
+        n = min(kFPages, min(gpe, t_end) - gp);
+        nw = (gp == gpb || gp == R0) ? 1 : 0;
+      }
+      dP[d] = gp;
+      dN[d] = n;
+      dB[d] = gb;
+      dS[d] = nw;
+      dJ[d] = gp - gpb;
+      dL[d] = gL;
+      gp += n;
+    };
+    auto load_id = [&](int is, int d) __attribute__((always_inline)) {
+      if (dN[d] > 0) last_idx = (size_t)dB[d] * a.P_max + (size_t)(dJ[d] + min(pr, dN[d] - 1));
+      iduse[is] = pr < dN[d];
+      size_t idx = last_idx;
+      asm volatile("" : "+v"(idx));  // a vector load (a scalar one would be waited for by every LDS wait)
+      idv[is] = a.bt[idx];
+    };
+    auto issue = [&](int bs, int is) __attribute__((always_inline)) {
+      const int phys = rfl(idv[is]);
+      const float* src = (iduse[is] ? kvf + (size_t)phys * kFPageFloats + qd_off
+                                    : reinterpret_cast<const float*>(g_zero_page)) + (size_t)lane * 4;
+#pragma unroll
+      for (int i = 0; i < kFLoads; ++i) buf[bs][i] = ld16_stream(src + (size_t)i * 256);
+    };
+    auto compute = [&](int bs, int d) __attribute__((always_inline)) -> bool {
+      const int P = dP[d], n = dN[d], b = dB[d];
+      const int L = dL[d];
+      const int j = dJ[d] + pr;  // this page slot's page within sequence b
+      f64x4 s2[2] = {f64x4{0.0, 0.0, 0.0, 0.0}, f64x4{0.0, 0.0, 0.0, 0.0}};
+      {
+        uint4 qv[kFLoads];
+#pragma unroll
+        for (int i = 0; i < kFLoads; ++i) qv[i] = s_q[qd][i][lane];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kFLoads; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s2[e & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)__uint_as_float(u4_get(buf[bs][i], e)),
+                                                             (double)__uint_as_float(u4_get(qv[i], e)), s2[e & 1],
+                                                             0, 0, 0);
+      }
+      s_part[xb][wv][lane] = s2[0] + s2[1];
+      const bool edge = pr < n && (j + 1) * kPage > L;  // rare: the sequence's last page
+      const bool zero_row = edge && j * kPage + tk >= L;  // this lane's token is not visible
+#pragma unroll
+      for (int i = 0; i < kFLoads; ++i)
+        *reinterpret_cast<uint4*>(vs + vw_row + (((4 * i + g) ^ tk) << 2)) =
+            zero_row ? make_uint4(0u, 0u, 0u, 0u) : buf[bs][i];  // 0 * NaN would poison the sum
+      __syncthreads();
+      const f64x4 s = ((s_part[xb][4 * pr][lane] + s_part[xb][4 * pr + 1][lane]) + s_part[xb][4 * pr + 2][lane]) +
+                      s_part[xb][4 * pr + 3][lane];
+      xb ^= 1;
+      if (n == 0) return false;  // past the end: the open segment is flushed after the loop
+      if (!seg_active) {
+        seg_active = true;
+        seg_b = b;
+        seg_first = P;
+      }
+      seg_end = P + n;
+      if (pr < n) {
+        double sn[4];  // scores of tokens g + 4e (natural units), -inf where not visible
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sn[e] = s[e];
+        if (edge) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j * kPage + g + 4 * e >= L) sn[e] = -INFINITY;
+        }
+        // Lazy rescaling as in the bf16 kernel, with a reference m_run (log2
+        // units, an fp32 value) at most kFRescale below the scores; the
+        // exponent s log2 e - m_run of a weight is formed in fp64 and rounded
+        // once, to a number below kFRescale.
+        const float lmax = (float)(fmax(fmax(sn[0], sn[1]), fmax(sn[2], sn[3])) * kLog2e64);
+        if (__any(lmax > m_run + kFRescale)) {
+          float mp = fmaxf(lmax, xor16(lmax));
+          mp = fmaxf(mp, xor32(mp));
+          const float m_new = (mp > m_run + kFRescale) ? mp : m_run;
+          const float alpha = exp2_fast(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+#pragma unroll
+          for (int t = 0; t < kFTiles; ++t) acc[t] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = exp2_fast((float)__builtin_fma(sn[e], kLog2e64, -(double)m_run));  // 0 where sn = -inf
+          l_run += p[e];
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < kFTiles / 4; ++q4) {
+          f32x4 v[4];
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int T = 4 * s4 + g;
+            v[s4] = *reinterpret_cast<const f32x4*>(vs + T * kFSlice + (((16 * q4 + tk) ^ T) << 2));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[4 * q4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[s4][e], p[s4], acc[4 * q4 + e], 0, 0, 0);
+        }
+      }
+      const int dn = (d + 1) % kGDesc;
+      if (dS[dn]) {  // the next step opens another segment: finish this one
+        flush();
+        load_q(dB[dn]);
+      }
+      return true;
+    };
+
+#pragma unroll
+    for (int d = 0; d < 4; ++d) gen(d);
+    reset_state();
+    load_q(dB[0]);
+    load_id(0, 0);
+    load_id(1, 1);
+    load_id(2, 2);
+    issue(0, 0);
+    issue(1, 1);
+    load_id(0, 3);
+    for (;;) {
+#pragma unroll
+      for (int u = 0; u < kGDesc; ++u) {
+        gen((u + 4) % kGDesc);
+        load_id((u + 4) % kGBuf, (u + 4) % kGDesc);
+        issue((u + 2) % kGBuf, (u + 2) % kGBuf);
+        if (!compute(u % kGBuf, u)) goto range_done;
+      }
+    }
+  range_done:
+    wait_vmem_all();
+    if (seg_active) flush();
+  }
+}
+
 // Log-sum-exp merge of the partial results of split sequences. Workgroup:
 // (sequence b, output tile T = 16 coordinates of all 16 heads, i.e. one
 // lane-order tile of a partial slot, or with LW = 16 a quarter of it: 4
@@ -885,7 +1232,9 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   a.B = s.batch;
   a.P_max = s.max_pages_per_seq;
   a.G = num_splits;
-  if (w_k)
+  if (s.kv_dtype == DA_DTYPE_F32)
+    hipLaunchKernelGGL(global_decode_f32_kernel, dim3((unsigned)num_splits), dim3(kFThreads), 0, stream, a);
+  else if (w_k)
     hipLaunchKernelGGL(global_decode_kernel<true>, dim3((unsigned)num_splits), dim3(kGThreads), 0, stream, a);
   else if (trace)
     hipLaunchKernelGGL((global_decode_kernel<false, true>), dim3((unsigned)num_splits), dim3(kGThreads), 0, stream,

@@ -130,8 +130,11 @@ da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* byte
 /*
  * decodeGQA over a paged K=V cache (Gemma-4-12B global layers: Hkv = 1,
  * G = 16, D = 512, values equal keys).
- *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16; out fp32 or bf16
- *   (shape->out_dtype; the split pieces are merged in fp32 and rounded once);
+ *   Built shapes: Hkv = 1, G = 16, D = 512; kv dtype bf16 or fp32 (q in the
+ *   same dtype; fp32 caches run a kernel whose scores are summed in fp64 and
+ *   whose weights and PV products are fp32, for results within 1e-5); out
+ *   fp32 or bf16 (shape->out_dtype; the split pieces are merged in fp32 and
+ *   rounded once);
  *   batch <= 256 (larger batches return DA_ERR_UNSUPPORTED; split them into
  *   calls of at most 256 sequences); num_splits <= 65536.
  *   Work split: the cached pages of the batch are divided into equal,
@@ -186,8 +189,9 @@ da_status attn_decode_global_noalloc(const void* q, const void* kv_cache, const 
  *             [t%16][d%8] with B = d/32 (each 32-coordinate block B in half
  *             B%2, so the pair (d, d + 256) shares a chunk slot of one half).
  *   w_k     : fp32 [512] device array, the k-norm weight.
- *   Everything else (shape limits, workspace, out, NaN in unread storage)
- *   as for attn_decode_global; the workspace size is the same.
+ *   shape->kv_dtype must be BF16 (DA_ERR_UNSUPPORTED otherwise). Everything
+ *   else (shape limits, workspace, out, NaN in unread storage) as for
+ *   attn_decode_global; the workspace size is the same.
  */
 da_status attn_decode_global_prenorm(const void* q, const void* x_cache, const float* w_k,
                                      const int32_t* block_table, const int32_t* seq_lens, void* out,

@@ -29,7 +29,8 @@ extern "C" {
  *   [3] bits 0..31: pages in its range; bits 32..63: the HW_ID register of
  *       its first wave (CU, SIMD, shader engine).
  * trace: device memory of at least 32 * splits bytes, caller-owned. A NULL
- * trace is an invalid argument.
+ * trace is an invalid argument. Built for bf16 caches only (an fp32 cache
+ * returns DA_ERR_UNSUPPORTED).
  */
 da_status attn_decode_global_traced(const void* q, const void* kv_cache, const int32_t* block_table,
                                     const int32_t* seq_lens, void* out, const da_shape* shape,

@@ -160,8 +160,28 @@ def test_global_validation(lib):
     assert glob(lib, _gshape(batch=-1)) == -1
     assert glob(lib, _gshape(), ptrs=[FAKE, NULL, FAKE, FAKE, FAKE]) == -1
     assert glob(lib, _gshape(group=8)) == -2
-    assert glob(lib, _gshape(kv_dtype=B.DA_DTYPE_F32)) == -2
     assert glob(lib, _gshape(batch=5000)) == -2
+
+
+def traced(lib, shape):
+    from decode_attention_amd import trace as T
+    T._lib()  # argument types of the traced entry point
+    return lib.attn_decode_global_traced(FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(shape), FAKE, 1 << 30, FAKE,
+                                         NULL)
+
+
+def test_global_fp32_cache_is_valid_except_for_the_timeline(lib):
+    # fp32 K=V caches run the fp32 kernel; the traced instance is bf16 only
+    assert traced(lib, _gshape(kv_dtype=B.DA_DTYPE_F32)) == -2
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
+def test_global_fp32_cache_reaches_the_device_check(lib):
+    f32 = _gshape(kv_dtype=B.DA_DTYPE_F32)
+    assert glob(lib, f32) == -4
+    assert glob_noalloc(lib, f32) == -4
+    assert global_gated(lib, f32) == -4
+    assert traced(lib, _gshape()) == -4
 
 
 def glob_noalloc(lib, shape, ptrs=None):

@@ -11,6 +11,8 @@ benchmark times, built by the same seeded generators:
   sliding_b64         sliding layer (window 1024), the same lengths
   long_context        global layer, B = 2, lengths 131072 and 262144
   prenorm_b64         global layer from the pre-norm projection, B = 64
+  global_b64_f32      global layer, B = 64, the same lengths, fp32 K=V cache
+                        (global_b64's bf16 values widened on the device)
   mq_verify_global    8 queries per sequence (speculative verification),
   mq_verify_sliding     B = 64, the decode workloads' lengths
   mq_prefill_global   one 2048-token prefill chunk per sequence, B = 4
@@ -22,8 +24,8 @@ import sys
 
 import numpy as np
 
-WORKLOADS = ("global_b64", "sliding_b64", "long_context", "prenorm_b64", "mq_verify_global", "mq_verify_sliding",
-             "mq_prefill_global", "mq_prefill_sliding")
+WORKLOADS = ("global_b64", "sliding_b64", "long_context", "prenorm_b64", "global_b64_f32", "mq_verify_global",
+             "mq_verify_sliding", "mq_prefill_global", "mq_prefill_sliding")
 
 
 def _dev(a):
@@ -39,12 +41,22 @@ def build_call(name):
     import torch
     import decode_attention_amd as da
     from . import inputs as I
-    if name in ("global_b64", "sliding_b64", "prenorm_b64") or name.startswith("mq_"):
+    if name in ("global_b64", "sliding_b64", "prenorm_b64", "global_b64_f32") or name.startswith("mq_"):
         sl, gl = I.config_workload(1), I.config_workload(2)
     if name == "global_b64":
         args = [_dev(x) for x in (gl.q, gl.kv_cache, gl.block_table, gl.seq_lens)]
         out = torch.empty((64, 16, 512), dtype=torch.float32, device="cuda")
         return lambda: da.attn_decode_global(*args, out=out)
+    if name == "global_b64_f32":
+        q, kv, bt, sl = (_dev(x) for x in (gl.q, gl.kv_cache, gl.block_table, gl.seq_lens))
+        P = kv.shape[0]
+        # tiled bf16 [P][1][64][16][8] -> tiled fp32 [P][1][128][16][4]: chunk c
+        # of 8 coordinates becomes chunks 2c and 2c + 1 of 4
+        kv32 = kv.float().view(P, 1, 64, 16, 2, 4).permute(0, 1, 2, 4, 3, 5).reshape(P, 1, 128, 16, 4).contiguous()
+        del kv
+        q32 = q.float()
+        out = torch.empty((64, 16, 512), dtype=torch.float32, device="cuda")
+        return lambda: da.attn_decode_global(q32, kv32, bt, sl, out=out)
     if name == "sliding_b64":
         args = [_dev(x) for x in (sl.q, sl.k_cache, sl.v_cache, sl.block_table, sl.seq_lens)]
         out = torch.empty((64, 16, 256), dtype=torch.float32, device="cuda")
