@@ -34,11 +34,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 # kernel sources they were taken on (hash below); reported as null otherwise.
 GLOBAL_TRAFFIC = {
     "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
-    "sha256": "225eab56bc10b07bacd49ce830a56bde3890954528e780c54e135d10f027944e",
-    "bytes_per_call": 1172767539,
+    "sha256": "1167b39e72df0ccd8805d4d5d0e7873c8070158377e17876272848d87fa76df5",
+    "bytes_per_call": 1172674150,
     # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) of
     # global_decode_kernel, from a third --pmc pass over the same sources
-    "mfma_busy": 0.1199,
+    "mfma_busy": 0.1200,
 }
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 
