@@ -315,8 +315,14 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
     q_ag = torch.empty((64, 16, 512), dtype=torch.bfloat16, device="cuda")
     gate_sl = to_dev(I.make_gate(sl.q.shape, tag=(702,)))
     gate_gl = to_dev(I.make_gate(gl.q.shape, tag=(703,)))
-    app_sl_us = time_calls(lambda: da.attn_kv_append_sliding(*d_as, q_out=q_as), n_extra)
-    app_gl_us = time_calls(lambda: da.attn_kv_append_global(*d_ag, q_out=q_ag), n_extra)
+    # bound calls (arguments checked once, as a serving loop would issue
+    # them), and the same calls through the checked Python path
+    run_as, _ = da.bind(da.attn_kv_append_sliding, *d_as, q_out=q_as)
+    run_ag, _ = da.bind(da.attn_kv_append_global, *d_ag, q_out=q_ag)
+    app_sl_us = time_calls(run_as, n_extra)
+    app_gl_us = time_calls(run_ag, n_extra)
+    app_sl_checked_us = time_calls(lambda: da.attn_kv_append_sliding(*d_as, q_out=q_as), n_extra)
+    app_gl_checked_us = time_calls(lambda: da.attn_kv_append_global(*d_ag, q_out=q_ag), n_extra)
     gsl_us = time_calls(lambda: da.attn_decode_sliding_gated(*d_sl[:5], sl.window, gate_sl, out=out_sl), n_extra)
     ggl_us = time_calls(lambda: da.attn_decode_global_gated(*d_gl, gate_gl, out=out_gl,
                                                             num_splits=num_splits), n_extra)
@@ -377,12 +383,16 @@ def time_extras(da, I, sl, gl, d_sl, d_gl, out_sl, out_gl, sb, gb, n_extra, num_
         "append_sliding_GBps": round(append_bytes(aws) / (app_sl_us * 1e-6) / 1e9, 1),
         "append_global_us_per_call": round(app_gl_us, 2),
         "append_global_GBps": round(append_bytes(awg) / (app_gl_us * 1e-6) / 1e9, 1),
+        "append_calls": "bound (da.bind: Python-side checks once, then the C call alone)",
+        "append_sliding_checked_us_per_call": round(app_sl_checked_us, 2),
+        "append_global_checked_us_per_call": round(app_gl_checked_us, 2),
         "sliding_gated_us_per_call": round(gsl_us, 2),
         "sliding_gated_GBps": round((sum(sb.values()) + gate_b * 256) / (gsl_us * 1e-6) / 1e9, 1),
         "global_gated_us_per_call": round(ggl_us, 2),
         "global_gated_GBps": round((sum(gb.values()) + gate_b * 512) / (ggl_us * 1e-6) / 1e9, 1),
     }
-    log(f"append sliding {app_sl_us:.1f} us, append global {app_gl_us:.1f} us, "
+    log(f"append sliding {app_sl_us:.1f} us ({app_sl_checked_us:.1f} checked), append global {app_gl_us:.1f} us "
+        f"({app_gl_checked_us:.1f} checked), "
         f"gated sliding {gsl_us:.1f} us, gated global {ggl_us:.1f} us")
 
     return extra

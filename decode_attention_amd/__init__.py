@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     attn_multiquery_global,
     attn_multiquery_workspace_bytes,
     attn_status_string,
+    bind,
     library_path,
     load_library,
 )

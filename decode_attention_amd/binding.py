@@ -118,6 +118,53 @@ def _check(status):
         raise DecodeAttnError(status, attn_status_string(status))
 
 
+_capture = threading.local()
+
+
+def _call(cfunc, *args):
+    """Issues one library call (a kernel launch), or records it while bind()
+    prepares a bound call."""
+    rec = getattr(_capture, "rec", None)
+    if rec is not None:
+        rec.append((cfunc, args))
+        return
+    _check(cfunc(*args))
+
+
+def bind(fn, *args, **kwargs):
+    """Prepares a call for a loop that repeats it on the same tensors.
+
+    Runs fn(*args, **kwargs), one of this module's calls, with its argument
+    checks and conversions, records the library call(s) it makes instead of
+    issuing them, and returns (run, result). result is what fn returns (keep
+    it, and every tensor passed, alive while run is used). run() issues the
+    same library call(s) again, with the same device pointers, shape and
+    stream, skipping the Python-side checks. The library still validates
+    its arguments on each call. The caller must not resize, free or
+    reallocate the tensors, and should use the stream that was current at
+    bind time, or the one passed. run is issued once before bind returns.
+    """
+    if getattr(_capture, "rec", None) is not None:
+        raise DecodeAttnError(-1, "bind() calls do not nest")
+    _capture.rec = []
+    try:
+        result = fn(*args, **kwargs)
+        rec = _capture.rec
+    finally:
+        _capture.rec = None
+    if not rec:
+        raise DecodeAttnError(-1, "the call issued no library call to bind")
+
+    def run():
+        for cfunc, a in rec:
+            st = cfunc(*a)
+            if st != DA_OK:
+                raise DecodeAttnError(st, attn_status_string(st))
+
+    run()
+    return run, result
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.float32:
@@ -208,14 +255,14 @@ def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stre
     out, out_dtype = _decode_out(out, (B, Hq, D), q.device)
     shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), out_dtype=out_dtype)
     if gate is None:
-        _check(lib.attn_decode_sliding(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                       _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),
-                                       _stream(stream)))
+        _call(lib.attn_decode_sliding, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+              _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),
+              _stream(stream))
     else:
         _check_gate(gate, out)
-        _check(lib.attn_decode_sliding_gated(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                             _ptr(seq_lens), int(window), _ptr(gate), _ptr(out),
-                                             ctypes.byref(shape), _stream(stream)))
+        _call(lib.attn_decode_sliding_gated, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+              _ptr(seq_lens), int(window), _ptr(gate), _ptr(out),
+              ctypes.byref(shape), _stream(stream))
     return out
 
 
@@ -254,8 +301,8 @@ def attn_decode_global_noalloc(q, kv_cache, block_table, seq_lens, out, num_spli
     _require(out is not None, "out is required")
     out, out_dtype = _decode_out(out, tuple(q.shape), q.device)
     shape = _global_shape(q, kv_cache, block_table, num_splits, out_dtype)
-    _check(lib.attn_decode_global_noalloc(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
-                                          _ptr(out), ctypes.byref(shape), _stream(stream)))
+    _call(lib.attn_decode_global_noalloc, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+          _ptr(out), ctypes.byref(shape), _stream(stream))
     return out
 
 
@@ -294,15 +341,15 @@ def _global(q, kv_cache, block_table, seq_lens, gate, out, workspace, num_splits
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if w_k is not None:
-        _check(lib.attn_decode_global_prenorm(_ptr(q), _ptr(kv_cache), _ptr(w_k), _ptr(block_table),
-                                              _ptr(seq_lens), _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st))
+        _call(lib.attn_decode_global_prenorm, _ptr(q), _ptr(kv_cache), _ptr(w_k), _ptr(block_table),
+              _ptr(seq_lens), _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st)
     elif gate is None:
-        _check(lib.attn_decode_global(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
-                                      ctypes.byref(shape), ws_ptr, ws_bytes, st))
+        _call(lib.attn_decode_global, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out),
+              ctypes.byref(shape), ws_ptr, ws_bytes, st)
     else:
         _check_gate(gate, out)
-        _check(lib.attn_decode_global_gated(_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
-                                            _ptr(gate), _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st))
+        _call(lib.attn_decode_global_gated, _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens),
+              _ptr(gate), _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st)
     return out
 
 
@@ -342,9 +389,9 @@ def attn_kv_append_sliding(q_raw, k_raw, v_raw, w_q, w_k, block_table, positions
     _require(q_out.dtype == k_cache.dtype and q_out.is_contiguous() and tuple(q_out.shape) == (B, Hq, D),
              "q_out must be contiguous [B, Hq, D] in the caches' dtype")
     shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(k_cache))
-    _check(lib.attn_kv_append_sliding(_ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(w_q), _ptr(w_k),
-                                      _ptr(block_table), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
-                                      _ptr(q_out), ctypes.byref(shape), _stream(stream)))
+    _call(lib.attn_kv_append_sliding, _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(w_q), _ptr(w_k),
+          _ptr(block_table), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+          _ptr(q_out), ctypes.byref(shape), _stream(stream))
     return q_out
 
 
@@ -375,9 +422,9 @@ def attn_kv_append_global(q_raw, kv_raw, w_q, w_k, block_table, positions, kv_ca
     _require(q_out.dtype == kv_cache.dtype and q_out.is_contiguous() and tuple(q_out.shape) == (B, Hq, D),
              "q_out must be contiguous [B, Hq, D] in the cache's dtype")
     shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(kv_cache))
-    _check(lib.attn_kv_append_global(_ptr(q_raw), _ptr(kv_raw), _ptr(w_q), _ptr(w_k), _ptr(block_table),
-                                     _ptr(positions), _ptr(kv_cache), _ptr(q_out), ctypes.byref(shape),
-                                     _stream(stream)))
+    _call(lib.attn_kv_append_global, _ptr(q_raw), _ptr(kv_raw), _ptr(w_q), _ptr(w_k), _ptr(block_table),
+          _ptr(positions), _ptr(kv_cache), _ptr(q_out), ctypes.byref(shape),
+          _stream(stream))
     return q_out
 
 
@@ -408,9 +455,9 @@ def attn_kv_append_global_prenorm(q_raw, x_raw, w_q, block_table, positions, x_c
     _require(q_out.dtype == torch.bfloat16 and q_out.is_contiguous() and tuple(q_out.shape) == (B, Hq, D),
              "q_out must be contiguous bf16 [B, Hq, D]")
     shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, DA_DTYPE_BF16)
-    _check(lib.attn_kv_append_global_prenorm(_ptr(q_raw), _ptr(x_raw), _ptr(w_q), _ptr(block_table),
-                                             _ptr(positions), _ptr(x_cache), _ptr(q_out), ctypes.byref(shape),
-                                             _stream(stream)))
+    _call(lib.attn_kv_append_global_prenorm, _ptr(q_raw), _ptr(x_raw), _ptr(w_q), _ptr(block_table),
+          _ptr(positions), _ptr(x_cache), _ptr(q_out), ctypes.byref(shape),
+          _stream(stream))
     return q_out
 
 
@@ -473,13 +520,13 @@ def _multiquery(sliding, q, q_start, max_queries, caches, block_table, seq_lens,
     ws_ptr = _ptr(workspace) if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if sliding:
-        _check(lib.attn_multiquery_sliding(_ptr(q), _ptr(q_start), int(max_queries), _ptr(caches[0]),
-                                           _ptr(caches[1]), _ptr(block_table), _ptr(seq_lens), int(window),
-                                           _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st))
+        _call(lib.attn_multiquery_sliding, _ptr(q), _ptr(q_start), int(max_queries), _ptr(caches[0]),
+              _ptr(caches[1]), _ptr(block_table), _ptr(seq_lens), int(window),
+              _ptr(out), ctypes.byref(shape), ws_ptr, ws_bytes, st)
     else:
-        _check(lib.attn_multiquery_global(_ptr(q), _ptr(q_start), int(max_queries), _ptr(caches[0]),
-                                          _ptr(block_table), _ptr(seq_lens), _ptr(out), ctypes.byref(shape),
-                                          ws_ptr, ws_bytes, st))
+        _call(lib.attn_multiquery_global, _ptr(q), _ptr(q_start), int(max_queries), _ptr(caches[0]),
+              _ptr(block_table), _ptr(seq_lens), _ptr(out), ctypes.byref(shape),
+              ws_ptr, ws_bytes, st)
     return out
 
 

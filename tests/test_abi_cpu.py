@@ -353,3 +353,36 @@ def test_probe_library_exports_and_validates():
     assert f(FAKE, FAKE, 4, 65536, FAKE, NULL) == -1
     assert f(ctypes.c_void_p(0x1008), FAKE, 4, 256, FAKE, NULL) == -1  # not 16-byte aligned
     assert f(FAKE, FAKE, 0, 256, FAKE, NULL) == 0  # nothing to read: nothing enqueued
+
+
+def test_bind_records_and_replays_the_library_calls():
+    # the mechanism alone, with a stand-in for a library function
+    from decode_attention_amd import binding as B
+    calls = []
+
+    def cfunc(*args):
+        calls.append(args)
+        return 0
+
+    def fn(x, y=0):
+        B._call(cfunc, x, y)
+        B._call(cfunc, y, x)
+        return "result"
+
+    run, result = B.bind(fn, 1, y=2)
+    assert result == "result"
+    assert calls == [(1, 2), (2, 1)]  # bind issues the recorded calls once
+    run()
+    run()
+    assert calls == [(1, 2), (2, 1)] * 3
+    with pytest.raises(B.DecodeAttnError):
+        B.bind(lambda: None)  # nothing to bind
+
+    def failing(*args):
+        return -2
+    run, _ = None, None
+    with pytest.raises(B.DecodeAttnError):
+        B.bind(lambda: B._call(failing))
+    with pytest.raises(B.DecodeAttnError):
+        B.bind(lambda: B.bind(fn, 1))  # no nesting
+    assert getattr(B._capture, "rec", None) is None
