@@ -229,21 +229,23 @@ def _check_gate(gate, out):
     _require(g0 + n <= o0 or o0 + n <= g0, "gate must not overlap out")
 
 
-def attn_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out=None, stream=None):
+def attn_decode_sliding(q, k_cache, v_cache, block_table, seq_lens, window, out=None, stream=None, num_splits=0):
     """slidingDecodeGQA. q [B, Hkv*G, D]; k_cache, v_cache [P, Hkv, 16, D]
     (row-major pages); block_table int32 [B, P_max]; seq_lens int32 [B].
     Returns out [B, Hkv*G, D]: fp32 (allocated if not given) or the given
-    fp32 or bf16 tensor."""
-    return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, None, out, stream)
+    fp32 or bf16 tensor. num_splits: waves each (sequence, KV head) window is
+    divided among (0: the default, 4; or 1, 2, 4, 8)."""
+    return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, None, out, stream, num_splits)
 
 
-def attn_decode_sliding_gated(q, k_cache, v_cache, block_table, seq_lens, window, gate, out=None, stream=None):
+def attn_decode_sliding_gated(q, k_cache, v_cache, block_table, seq_lens, window, gate, out=None, stream=None,
+                              num_splits=0):
     """attn_decode_sliding followed by sigmoidGate: out = o * sigmoid(gate),
     gate fp32 [B, Hkv*G, D]."""
-    return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stream)
+    return _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stream, num_splits)
 
 
-def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stream):
+def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stream, num_splits=0):
     import torch
     lib = load_library()
     _check_common(q, block_table, seq_lens, (k_cache, v_cache))
@@ -253,7 +255,8 @@ def _sliding(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, stre
     P, Hkv, _, Dk = k_cache.shape
     _require(Dk == D and Hq % Hkv == 0, "head shape mismatch")
     out, out_dtype = _decode_out(out, (B, Hq, D), q.device)
-    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), out_dtype=out_dtype)
+    shape = make_shape(B, Hkv, Hq // Hkv, D, block_table.shape[1], P, _dtype_code(q), num_splits=num_splits,
+                       out_dtype=out_dtype)
     if gate is None:
         _call(lib.attn_decode_sliding, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
               _ptr(seq_lens), int(window), _ptr(out), ctypes.byref(shape),

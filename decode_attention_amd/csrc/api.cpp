@@ -82,6 +82,11 @@ da_status decode_sliding(const void* q, const void* k_cache, const void* v_cache
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out) return DA_ERR_INVALID_ARG;
   if (window < 0) return DA_ERR_INVALID_ARG;
   if (shape->group != 2 || shape->head_dim != 256) return DA_ERR_UNSUPPORTED;
+  // waves per (sequence, KV head): 0 (the default, 4), or 1, 2, 4 or 8 (8
+  // with bf16 caches only)
+  const int ns = shape->num_splits;
+  if (ns != 0 && ns != 1 && ns != 2 && ns != 4 && ns != 8) return DA_ERR_UNSUPPORTED;
+  if (ns == 8 && shape->kv_dtype != DA_DTYPE_BF16) return DA_ERR_UNSUPPORTED;
   if ((long long)shape->batch * shape->num_kv_heads > 0x7FFFFFFFLL) return DA_ERR_UNSUPPORTED;
   int dev = 0, cus = 0;
   st = current_device(&dev, &cus);

@@ -71,6 +71,17 @@ __device__ __forceinline__ float chunk_dot<float>(const uint4& qv, const uint4& 
   return fmaf(__uint_as_float(qv.w), __uint_as_float(kv.w), s);
 }
 
+// fp32 caches: the same dot product in fp64 (exact products of the fp32
+// values, fp64 sums), so that the scores carry no fp32 rounding into the
+// weights (see the kernel).
+__device__ __forceinline__ double chunk_dot_f64(const uint4& qv, const uint4& kv) {
+  double s = (double)__uint_as_float(qv.x) * (double)__uint_as_float(kv.x);
+  s = __builtin_fma((double)__uint_as_float(qv.y), (double)__uint_as_float(kv.y), s);
+  s = __builtin_fma((double)__uint_as_float(qv.z), (double)__uint_as_float(kv.z), s);
+  return __builtin_fma((double)__uint_as_float(qv.w), (double)__uint_as_float(kv.w), s);
+}
+constexpr double kSlLog2e64 = 1.4426950408889634074;
+
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
@@ -148,32 +159,61 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
   auto compute = [&](int buf, int k) {
     const int t0 = (j_lo + wv + NW * k) * kPage;
     const bool edge = (t0 < lo) || (t0 + kPage > L);
-    float s[NI];
+    // scores of this lane's head (even 16-lane rows: head 0, odd: head 1):
+    // bf16, fp32 in log2 units; fp32 caches, fp64 in natural units (at
+    // D = 256 fp32 sums alone move the scores by up to ~1e-5 relative to
+    // the weights' tolerance)
+    constexpr bool kF64 = sizeof(T) == 4;
+    float s[kF64 ? 1 : NI];
+    double sd[kF64 ? NI : 1];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const float p0 = chunk_dot<T>(q0, kb[buf][i]);
-      const float p1 = chunk_dot<T>(q1, kb[buf][i]);
-      const f2 r = swap16(p0, p1);  // even rows: head 0, odd rows: head 1
-      float u = row_sum16(r.a + r.b);
-      if constexpr (TPI == 1) {
-        const f2 h = swap32(u, u);
-        u = h.a + h.b;
+      if constexpr (kF64) {
+        // a token spans the wave: fixed xor butterfly over all 64 lanes, in
+        // fp64 (commutative steps: every lane ends with the same sums)
+        double t0 = chunk_dot_f64(q0, kb[buf][i]), t1 = chunk_dot_f64(q1, kb[buf][i]);
+#pragma unroll
+        for (int off = kWave / 2; off >= 1; off >>= 1) {
+          t0 += __shfl_xor(t0, off);
+          t1 += __shfl_xor(t1, off);
+        }
+        sd[i] = ((lane >> 4) & 1) ? t1 : t0;
+      } else {
+        const float p0 = chunk_dot<T>(q0, kb[buf][i]);
+        const float p1 = chunk_dot<T>(q1, kb[buf][i]);
+        const f2 r = swap16(p0, p1);  // even rows: head 0, odd rows: head 1
+        float u = row_sum16(r.a + r.b);
+        if constexpr (TPI == 1) {
+          const f2 h = swap32(u, u);
+          u = h.a + h.b;
+        }
+        s[i] = u * kLog2e;
       }
-      s[i] = u * kLog2e;
     }
     if (edge) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int pos = t0 + i * TPI + tt;
         if (pos < lo || pos >= L) {
-          s[i] = -INFINITY;
+          if constexpr (kF64)
+            sd[i] = -INFINITY;
+          else
+            s[i] = -INFINITY;
           vb[buf][i] = make_uint4(0u, 0u, 0u, 0u);  // 0 * NaN would poison the sum
         }
       }
     }
-    float mp = s[0];
+    float mp;
+    if constexpr (kF64) {
+      double md = sd[0];
 #pragma unroll
-    for (int i = 1; i < NI; ++i) mp = fmaxf(mp, s[i]);
+      for (int i = 1; i < NI; ++i) md = fmax(md, sd[i]);
+      mp = (float)(md * kSlLog2e64);
+    } else {
+      mp = s[0];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mp = fmaxf(mp, s[i]);
+    }
     if constexpr (TPI == 2) mp = fmaxf(mp, xor32(mp));
     const float m_new = fmaxf(m_run, mp);  // finite: every page has a visible key
     const float alpha = exp2_fast(m_run - m_new);
@@ -187,7 +227,9 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const float p = exp2_fast(s[i] - m_new);
+      // (fp32 caches: the exponent s log2 e - m formed in fp64, rounded once)
+      const float p = kF64 ? exp2_fast((float)__builtin_fma(sd[kF64 ? i : 0], kSlLog2e64, -(double)m_new))
+                           : exp2_fast(s[kF64 ? 0 : i] - m_new);
       l_run += p;
       const f2 pp = swap16(p, p);  // .a head 0, .b head 1, same token
       float v[E];
@@ -260,24 +302,45 @@ __global__ __launch_bounds__(NW * kWave) void sliding_decode_kernel(
   }
 }
 
-constexpr int kSlidingWaves = 4;
+constexpr int kSlidingWaves = 4;  // default waves per (sequence, KV head)
+
+template <typename T, int NW>
+static void launch_sliding_nw(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t window, const float* gate, void* out, int out_bf16,
+                              const da_shape& s, hipStream_t stream) {
+  hipLaunchKernelGGL((sliding_decode_kernel<T, 256, NW>), dim3((unsigned)s.batch * (unsigned)s.num_kv_heads),
+                     dim3(NW * kWave), 0, stream, (const T*)q, (const T*)k_cache, (const T*)v_cache, block_table,
+                     seq_lens, window, gate, out, out_bf16, s.num_kv_heads, s.max_pages_per_seq);
+}
+
+template <typename T>
+static void launch_sliding_t(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                             const int32_t* seq_lens, int32_t window, const float* gate, void* out, int out_bf16,
+                             const da_shape& s, hipStream_t stream) {
+  // s.num_splits: waves a unit's window is divided among (0: the default);
+  // the API has admitted only 0, 1, 2, 4 and 8 (8 with bf16 caches only)
+  switch (s.num_splits == 0 ? kSlidingWaves : s.num_splits) {
+    case 1: launch_sliding_nw<T, 1>(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, out_bf16, s,
+                                    stream); break;
+    case 2: launch_sliding_nw<T, 2>(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, out_bf16, s,
+                                    stream); break;
+    case 8:  // bf16 only: the fp32 kernel's registers exceed 2 waves per SIMD
+      if constexpr (sizeof(T) == 2)
+        launch_sliding_nw<T, 8>(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, out_bf16, s, stream);
+      break;
+    default: launch_sliding_nw<T, 4>(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, out_bf16, s,
+                                     stream); break;
+  }
+}
 
 da_status launch_sliding(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, const int32_t* seq_lens, int32_t window, const float* gate,
                          void* out, const da_shape& s, hipStream_t stream) {
-  const dim3 grid((unsigned)s.batch * (unsigned)s.num_kv_heads);
-  const dim3 block(kSlidingWaves * kWave);
   const int out_bf16 = s.out_dtype == DA_DTYPE_BF16 ? 1 : 0;
-  if (s.kv_dtype == DA_DTYPE_BF16) {
-    hipLaunchKernelGGL((sliding_decode_kernel<uint16_t, 256, kSlidingWaves>), grid, block, 0, stream,
-                       (const uint16_t*)q, (const uint16_t*)k_cache, (const uint16_t*)v_cache,
-                       block_table, seq_lens, window, gate, out, out_bf16, s.num_kv_heads,
-                       s.max_pages_per_seq);
-  } else {
-    hipLaunchKernelGGL((sliding_decode_kernel<float, 256, kSlidingWaves>), grid, block, 0, stream,
-                       (const float*)q, (const float*)k_cache, (const float*)v_cache, block_table,
-                       seq_lens, window, gate, out, out_bf16, s.num_kv_heads, s.max_pages_per_seq);
-  }
+  if (s.kv_dtype == DA_DTYPE_BF16)
+    launch_sliding_t<uint16_t>(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, out_bf16, s, stream);
+  else
+    launch_sliding_t<float>(q, k_cache, v_cache, block_table, seq_lens, window, gate, out, out_bf16, s, stream);
   return hipGetLastError() == hipSuccess ? DA_OK : DA_ERR_LAUNCH;
 }
 

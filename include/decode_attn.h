@@ -100,8 +100,12 @@ typedef struct da_shape {
                                 the appends take DA_DTYPE_F32 only */
   int32_t num_splits;        /* attn_decode_global: number of workgroups the
                                 cached pages of the whole batch are divided
-                                among (0 = one per compute unit); ignored by
-                                attn_decode_sliding */
+                                among (0 = one per compute unit).
+                                attn_decode_sliding: number of waves each
+                                (sequence, KV head) window is divided among,
+                                page by page, their states merged in LDS:
+                                0 (the default, 4), 1, 2, 4 or 8 (8 with bf16
+                                caches only) */
 } da_shape;
 
 /*
@@ -110,6 +114,10 @@ typedef struct da_shape {
  *   Built shapes: (Hkv, G, D) with G = 2, D = 256, any Hkv >= 1;
  *   kv dtypes fp32 and bf16; out fp32 or bf16 (shape->out_dtype).
  *   window >= 0 (0 gives zeros). seq_lens: int32 [batch].
+ *   shape->num_splits: 0, 1, 2, 4 or 8 (waves per sequence and KV head,
+ *   above; 8 with bf16 caches only); other values return
+ *   DA_ERR_UNSUPPORTED. The results of
+ *   different wave counts agree to fp32 rounding.
  * Returns DA_OK, DA_ERR_INVALID_ARG, DA_ERR_UNSUPPORTED, DA_ERR_NO_DEVICE or
  * DA_ERR_LAUNCH.
  */

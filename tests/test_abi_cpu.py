@@ -117,6 +117,9 @@ def test_sliding_validation(lib):
     assert sliding(lib, _shape(), ptrs=[FAKE, FAKE, NULL, FAKE, FAKE, FAKE]) == -1
     assert sliding(lib, _shape(head_dim=128)) == -2
     assert sliding(lib, _shape(group=4)) == -2
+    for ns in (3, 5, 16):  # waves per unit: 0, 1, 2, 4 or 8 only
+        assert sliding(lib, _shape(num_splits=ns)) == -2
+    assert sliding(lib, _shape(num_splits=8, kv_dtype=B.DA_DTYPE_F32)) == -2  # 8: bf16 only
     s = _shape()
     s.page_size = 32
     assert sliding(lib, s) == -2
@@ -210,6 +213,8 @@ def test_workspace_bytes_with_explicit_splits(lib):
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
 def test_no_device_reported_after_valid_arguments(lib):
     assert sliding(lib, _shape()) == -4
+    for ns in (1, 2, 4, 8):
+        assert sliding(lib, _shape(num_splits=ns)) == -4
     assert glob(lib, _gshape()) == -4
     n = ctypes.c_size_t(0)
     assert lib.attn_decode_global_workspace_bytes(ctypes.byref(_gshape()), ctypes.byref(n)) == -4

@@ -119,3 +119,32 @@ def test_head_isolation_and_read_only(gpu_lib):
     others = [h for h in range(16) if h not in heads_c3]
     assert torch.equal(pert[:, others], base[:, others])
     assert not torch.equal(pert[:, heads_c3], base[:, heads_c3])
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_invariant_to_waves_per_unit(gpu_lib, kv_dtype):
+    # The window of each (sequence, KV head) is divided among 1, 2, 4 or (bf16)
+    # 8 waves, page by page, whose states are merged in LDS: every wave count
+    # matches the oracle, the counts agree to fp32 rounding of the merge, and
+    # each repeats bit for bit (a race in the LDS merge would show in one of
+    # the three)
+    wl = I.make_sliding(EDGE_LENS, kv_dtype=kv_dtype, tag=(1600,), **I.SLIDING)
+    ref = oracle.paged_decode_sliding(wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens, wl.window,
+                                      wl.kv_dtype)
+    args = [dev(x) for x in (wl.q, wl.k_cache, wl.v_cache, wl.block_table, wl.seq_lens)]
+    import decode_attention_amd as da
+    outs = {}
+    counts = (1, 2, 4, 8) if kv_dtype == "bf16" else (1, 2, 4)  # 8 waves: bf16 caches only
+    for nw in counts:
+        a = da.attn_decode_sliding(*args, wl.window, num_splits=nw)
+        b = da.attn_decode_sliding(*args, wl.window, num_splits=nw)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), nw
+        outs[nw] = a.cpu().numpy().astype(np.float64)
+        err = max_abs(outs[nw], ref)
+        print(f"[sliding] {kv_dtype}, {nw} waves per unit: max-abs error {err:.3e}", flush=True)
+        assert err <= tol(kv_dtype), (nw, err)
+    default = da.attn_decode_sliding(*args, wl.window).cpu().numpy().astype(np.float64)
+    assert np.array_equal(default, outs[4])
+    for nw in counts:
+        assert max_abs(outs[nw], outs[4]) <= 2e-6, nw
