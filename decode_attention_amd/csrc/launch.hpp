@@ -55,6 +55,7 @@ struct mq_plan {
   int balanced;     // 1: pieces per unit; 2: contiguous shares
   int nsplit;       // fixed split: pieces per unit (1: none)
   int grid;         // balanced: workgroups of the main kernel
+  int rows;         // rows per block: 128, or 256 (sliding layers, long chunks)
   size_t ws_bytes;  // workspace the call needs
 };
 mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_cus);

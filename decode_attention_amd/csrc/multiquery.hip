@@ -14,7 +14,8 @@
 // sliding layers 64 queries (mq_kernel, 8 waves of 16 rows x 256
 // coordinates), on global layers 8 queries (mq_global_kernel, below), so that
 // speculative verification of up to 8 draft tokens reads each sequence's
-// keys once.
+// keys once. Sliding calls with 128 or more queries in a sequence take
+// 256-row blocks of 32-row tiles instead (mq_sliding_kernel, below).
 //
 // Sliding (mq_kernel). The workgroup walks the pages that some row of its block can see,
 // two pages per step, staged in LDS (double-buffered), with the loads of the
@@ -90,11 +91,11 @@ struct MQArgs {
   int units, grid;          // balanced split: B*Hkv*nblk units over `grid` workgroups
 };
 
-template <int D, int G>
+template <int D, int G, int ROWS = 128>
 struct MQShape {
   static_assert((D == 256 && G == 2) || (D == 512 && G == 16), "built shapes");
   static constexpr bool kSliding = D == 256;
-  static constexpr int kRows = 128;                     // rows per workgroup
+  static constexpr int kRows = ROWS;                    // rows per workgroup
   static constexpr int kQueries = kRows / G;            // queries per workgroup
   static constexpr int kKPage = kSliding ? 8192 : 16384;  // LDS bytes per page of K (and of V)
   static constexpr int kVBase = kSliding ? kMRegion : 0;  // V region (global: V = K)
@@ -113,9 +114,9 @@ __device__ __forceinline__ T mq_sload(const T* p, long long i) {
 
 // Pages the rows of unit u = (sequence, KV head, row block) see, as the main
 // kernel walks them (0 for a block without rows).
-template <int D, int G>
+template <int D, int G, int ROWS = 128>
 __device__ int mq_unit_pages(const MQArgs& a, int u) {
-  using C = MQShape<D, G>;
+  using C = MQShape<D, G, ROWS>;
   const int blk = u % a.nblk, bc = u / a.nblk, b = bc / a.Hkv;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
@@ -211,13 +212,14 @@ __device__ T mq_block_exscan(T v, T* s_w, T& total) {
 // hdr = {steps, per}, off[u] (first step of unit u; off[units] = steps),
 // tab, and wfirst[w] (the unit holding workgroup w's first step; -1: w has
 // no steps).
+template <int D, int G, int ROWS>
 __global__ __launch_bounds__(kMPlanThreads) void mq_plan_contig_kernel(MQArgs a) {
   __shared__ long long s_w[kMPlanThreads / kWave];
   __shared__ int s_wi[kMPlanThreads / kWave];
   const int tid = threadIdx.x, U = a.units;
   const int per_t = (U + kMPlanThreads - 1) / kMPlanThreads;
   const int u0 = min(U, tid * per_t), u1 = min(U, u0 + per_t);
-  auto unit_steps = [&](int u) -> long long { return (mq_unit_pages<512, 16>(a, u) + 1) / 2; };
+  auto unit_steps = [&](int u) -> long long { return (mq_unit_pages<D, G, ROWS>(a, u) + 1) / 2; };
   long long loc = 0;
   for (int u = u0; u < u1; ++u) loc += unit_steps(u);
   long long tot;
@@ -875,14 +877,304 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   }  // pieces
 }
 
+// ---------------------------------------------------------------- sliding layers, long chunks
+// mq_sliding_kernel: the global kernel's 32-row tiles for the sliding layers,
+// used when a call has 128 or more queries in a sequence (prefill chunks).
+// 256 rows per workgroup: 128 queries x the 2 heads of one KV head, wave w
+// owning row tile w (32 rows) and all 256 coordinates, so no partial scores
+// are exchanged. K and V pages of the KV head go HBM -> LDS
+// (global_load_lds_dwordx4) in the global kernel's order (16-byte chunks of
+// 8 coordinates, chunk-major, slots XOR-swizzled by the chunk), the source
+// addresses picking each chunk out of the row-major page: per step the two
+// pages' K (2 x 8 KB) and V (2 x 8 KB), a ring of 4 steps (128 KB) loaded
+// three steps ahead. A lane whose token no row of the block sees (outside
+// [first query's position - window + 1, last query's position], or past the
+// piece) loads the zero page. Per step and wave: S^T (32 tokens x 32 rows)
+// with 16 x mfma_f32_32x32x16_bf16, masks (l <= p and l > p - window), the
+// one-pass softmax, and O^T (256 x 32) += V^T P^T with 16 more, as in the
+// global kernel. A step every row of a tile sees in full skips the mask.
+constexpr int kQSRows = 256;                 // rows per workgroup
+constexpr int kQSPage = 8192;                // bytes of one page of one KV head (16 x 256 bf16)
+constexpr int kQSStep = 4 * kQSPage;         // K and V of two pages
+constexpr int kQSVBase = 2 * kQSPage;        // the V pages' offset in a step
+constexpr int kQSDma = kQSStep / kMThreads / 16;  // 16-byte loads per thread and step (4)
+constexpr int kQSMinQueries = 128;           // calls with fewer queries per sequence use mq_kernel
+
+__global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) void mq_sliding_kernel(MQArgs a) {
+  using C = MQShape<256, 2, kQSRows>;
+  __shared__ __attribute__((aligned(16))) uint8_t s_k0[kQSStep];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k1[kQSStep];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k2[kQSStep];
+  __shared__ __attribute__((aligned(16))) uint8_t s_k3[kQSStep];
+
+  // The workgroup's pieces, as in mq_global_kernel.
+  const bool contig = a.balanced == 2;
+  long long g0 = 0, g1 = 0, per = 1;
+  int u = 0;
+  if (contig) {
+    const long long tot = mq_sload(a.hdr, 0);
+    per = mq_sload(a.hdr, 1);
+    g0 = (long long)blockIdx.x * per;
+    g1 = min(g0 + per, tot);
+    if (g0 >= g1) return;  // no steps for this workgroup
+    u = mq_sload(a.wfirst, blockIdx.x);
+  }
+  for (bool first = true;; first = false) {
+  int blk, bc, ja, jb, slot = -1;
+  long long ls0 = 0, ls1 = 0;
+  if (contig) {
+    if (g0 >= g1) break;
+    long long o0 = mq_sload(a.off, u), o1 = mq_sload(a.off, u + 1);
+    while (o1 <= g0) {  // units without steps
+      ++u;
+      o0 = o1;
+      o1 = mq_sload(a.off, u + 1);
+    }
+    const long long e = min(g1, o1);
+    ls0 = g0 - o0;
+    ls1 = e - o0;
+    const int t0 = mq_sload(a.tab, u);
+    if (mq_sload(a.tab, u + 1) > t0) slot = t0 + (int)((long long)blockIdx.x - o0 / per);
+    blk = u % a.nblk;
+    bc = u / a.nblk;
+    g0 = e;
+    ++u;
+  } else {
+    if (!first) break;
+    blk = blockIdx.x;
+    bc = blockIdx.z;
+    if (a.nsplit > 1) slot = (bc * a.nblk + blk) * a.nsplit + (int)blockIdx.y;
+  }
+  if (!first) {
+    // the previous piece's last step still reads the ring
+    __builtin_amdgcn_s_waitcnt(DA_WAIT_LGKM0);
+    qg_barrier();
+  }
+  const int b = bc / a.Hkv, c = bc - b * a.Hkv;
+  const int Hq = 2 * a.Hkv;
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
+  const int q0 = a.q_start[b];
+  const int S = a.q_start[b + 1] - q0;
+  const int s0 = blk * C::kQueries;
+  if (s0 >= S) continue;  // no rows in this block (the merge skips it too)
+  const int s1 = min(S, s0 + C::kQueries) - 1;
+  const int w = a.window;
+  const int khi = L - S + s1;                   // the last key any row sees
+  const int klo = max(0, L - S + s0 - w + 1);   // the first
+  const int jlo = klo / kPage;
+  const int np = (khi >= 0 && w > 0) ? khi / kPage - jlo + 1 : 0;  // pages of the block, from page jlo
+  if (contig) {
+    ja = (int)(2 * ls0);
+    jb = (int)min(2 * ls1, (long long)np);
+  } else {
+    ja = (int)((long long)blockIdx.y * np / a.nsplit);
+    jb = (int)((long long)(blockIdx.y + 1) * np / a.nsplit);
+  }
+  const int nsteps = (jb - ja + 1) / 2;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = mq_rfl(tid / kWave);
+  const int rt = wv;  // row tile
+  const int n = lane & 31, h = lane >> 5;
+  const int r_wg = 32 * rt + n;   // this lane's row (column of its tiles)
+  const int s_r = s0 + (r_wg >> 1);
+  const int gh = r_wg & 1;        // head within the KV head's group
+  const bool valid = s_r <= s1;
+  const int pos_r = valid ? L - S + s_r : -1;  // -1: sees nothing
+  const bool wact = s0 + 16 * rt <= s1;        // a tile holds 16 queries: its first one exists
+
+  // Q^T (B operand) for k-step i: row n, coordinates 16 i + 8 h .. +8
+  uint4 qv[16];
+  {
+    const uint16_t* qp = a.q + ((size_t)(q0 + s_r) * Hq + 2 * c + gh) * 256 + 8 * h;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qv[i] = valid ? ld16(qp + 16 * i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Loads of step k: wave w fills bytes [4w, 4w + 4) KB of the step's LDS
+  // region [K page 0][K page 1][V page 0][V page 1], i.e. half (w % 2) of
+  // page (w / 2) % 2 of K (w < 4) or V, 1 KB (four chunks of 16 tokens) per
+  // load. Slot p of chunk cc holds token p ^ 4 (cc % 4), so lane l of load u
+  // fetches chunk 16 (w % 2) + 4 u + l / 16, token (l % 16) ^ 4 (l / 16),
+  // from the row-major page (element 256 token + 8 chunk).
+  const int pg_w = (wv >> 1) & 1;
+  const int tok_w = (lane & 15) ^ (4 * (lane >> 4));
+  const int lane_src = tok_w * 256 + 8 * (16 * (wv & 1) + (lane >> 4));  // elements, + 32 u
+  const uint16_t* cache_w = wv < 4 ? a.k : a.v;
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_page);
+  auto load_id = [&](int k) __attribute__((always_inline)) -> int {
+    // wave-uniform: a scalar load, counted by lgkmcnt (the block table is
+    // read-only during the call: the constant address space lets the
+    // compiler use s_load)
+    const int j = jlo + min(ja + 2 * k + pg_w, max(jb - 1, 0));
+    const __attribute__((address_space(4))) int* bt = (const __attribute__((address_space(4))) int*)a.bt;
+    return bt[(size_t)b * a.P_max + j];
+  };
+  auto issue = [&](int k, int id, uint8_t* buf) __attribute__((always_inline)) {
+    const int jr = ja + 2 * k + pg_w;  // page within the block's range
+    const int pos = (jlo + jr) * kPage + tok_w;
+    const bool keep = jr < jb && pos >= klo && pos <= khi;
+    // (lane_src + 32 u stays below 4096 elements: inside the page, and inside
+    // the 16 KB zero page)
+    const uint16_t* src = (keep ? cache_w + ((size_t)mq_rfl(id) * a.Hkv + c) * (kPage * 256) : zero) + lane_src;
+    uint8_t* dst = buf + wv * (kQSDma * 1024);
+#pragma unroll
+    for (int uu = 0; uu < kQSDma; ++uu)
+      __builtin_amdgcn_global_load_lds(src + 32 * uu, (__attribute__((address_space(3))) void*)(dst + uu * 1024), 16,
+                                       0, 0);
+  };
+
+  f32x16 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // K reads (A operand): token n (page n / 16), chunk 2 i + h of k-step i,
+  // whose index mod 4 is h + 2 (i % 2): two base offsets, + 512 i.
+  const int k_base = (n >> 4) * kQSPage + h * 256;
+  const int k_off0 = k_base + (((n & 15) ^ (4 * h)) * 16);      // + 512 i, i even
+  const int k_off1 = k_base + (((n & 15) ^ (4 * h + 8)) * 16);  // + 512 i, i odd
+  // V^T reads, as in the global kernel (chunk 4 t + cl of page ks):
+  // + kQSVBase + kQSPage ks + 1024 t
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int cl = 2 * (g16 & 1) + ((i16 & 3) >> 1);
+  const int tr_off0 = cl * 256 + (((4 * (g16 >> 1) + (i16 >> 2)) ^ (4 * cl)) * 16) + (i16 & 1) * 8;
+  const int tr_off1 = tr_off0 ^ 128;
+  // The tile's rows see positions [pos_first - w + 1, pos_last] at least and
+  // at most [pos_last - w + 1, pos_first]: a step inside the latter needs no mask.
+  const int pos_first = L - S + s0 + 16 * rt, pos_last = pos_first + 15;
+
+  auto compute = [&](int k, const uint8_t* kb) __attribute__((always_inline)) {
+    if (!wact) return;
+    f32x16 x = {};
+    const uint32_t kb_addr = qg_lds_addr(kb);
+    const uint32_t ka0 = kb_addr + k_off0, ka1 = kb_addr + k_off1;
+    qg_static_for(std::make_integer_sequence<int, 8>{}, [&](auto bi) __attribute__((always_inline)) {
+      constexpr int I = 2 * decltype(bi)::value;
+      uint4 kv0, kv1;
+      qg_read_k2<I * 512, (I + 1) * 512>(ka0, ka1, kv0, kv1);
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv0), __builtin_bit_cast(bf16x8, qv[I]),
+                                                  x, 0, 0, 0);
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv1),
+                                                  __builtin_bit_cast(bf16x8, qv[I + 1]), x, 0, 0, 0);
+    });
+    const int jr0 = ja + 2 * k;
+    const int T0 = (jlo + jr0) * kPage;  // position of the step's first token
+    if (!(jr0 + 2 <= jb && T0 >= pos_last - w + 1 && T0 + 2 * kPage - 1 <= pos_first)) {
+      // element e = 4 c4 + jj holds token 8 c4 + 4 h + jj of the step (page of that / 16)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tok = 8 * (e >> 2) + 4 * h + (e & 3);
+        const int pos = T0 + tok;
+        if (!(jr0 + (tok >> 4) < jb && pos <= pos_r && pos > pos_r - w)) x[e] = -INFINITY;
+      }
+    }
+    float lmax = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lmax = fmaxf(lmax, x[e]);
+    lmax *= kLog2e;  // log2 units, as m_run
+    // lazy rescaling (as in the decode kernels)
+    if (__any(lmax > m_run + kMRescale)) {
+      const float mp = fmaxf(lmax, xor32(lmax));  // the row's max: lanes l and l ^ 32 hold its tokens
+      const float m_new = (mp > m_run + kMRescale) ? mp : m_run;
+      const float alpha = (m_new == m_run) ? 1.f : exp2_fast(m_run - m_new);  // 0 from -inf
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[t] *= alpha;
+    }
+    // m_run is -inf only while every score so far, this step's included, is -inf
+    const float mneg = m_run == -INFINITY ? 0.f : -m_run;
+    bf16x8 pp[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) pp[e >> 3][e & 7] = (__bf16)exp2_fast(__builtin_fmaf(x[e], kLog2e, mneg));  // 0 from -inf
+    // the denominator sums the weights as rounded for the PV product
+    const uint4 p0 = __builtin_bit_cast(uint4, pp[0]), p1 = __builtin_bit_cast(uint4, pp[1]);
+    constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+    l_run = dot2_bf16(p0.x, kOnes, dot2_bf16(p0.y, kOnes, dot2_bf16(p0.z, kOnes, dot2_bf16(p0.w, kOnes, l_run))));
+    l_run = dot2_bf16(p1.x, kOnes, dot2_bf16(p1.y, kOnes, dot2_bf16(p1.z, kOnes, dot2_bf16(p1.w, kOnes, l_run))));
+    const uint32_t va0 = kb_addr + tr_off0, va1 = kb_addr + tr_off1;
+    qg_static_for(std::make_integer_sequence<int, 8>{}, [&](auto bi) __attribute__((always_inline)) {
+      constexpr int ks = decltype(bi)::value >> 2, t0 = 2 * (decltype(bi)::value & 3);
+      s16x4 a0, a1, b0, b1;  // tiles t0 and t0 + 1, first and second read
+      qg_read_v2<kQSVBase + ks * kQSPage + t0 * 1024>(va0, va1, a0, a1, b0, b1);
+      acc[t0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7)), pp[ks], acc[t0], 0, 0, 0);
+      acc[t0 + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7)), pp[ks], acc[t0 + 1], 0,
+          0, 0);
+    });
+  };
+
+  // One step, as in mq_global_kernel: at most the pages of steps k + 1 and
+  // k + 2 (2 kQSDma loads) are in flight past the wait; past the barrier
+  // every wave's part of step k is in LDS and every wave is done with step
+  // k - 1, whose slot then takes step k + 3.
+  int id_n = 0;  // id of step k + 3
+  auto step = [&](int k, const uint8_t* cur, uint8_t* nxt3) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(2 * kQSDma));
+    qg_barrier();
+    issue(k + 3, id_n, nxt3);
+    id_n = load_id(k + 4);
+    compute(k, cur);
+  };
+  if (nsteps > 0) {
+    const int id0 = load_id(0), id1 = load_id(1), id2 = load_id(2);
+    id_n = load_id(3);
+    issue(0, id0, s_k0);
+    issue(1, id1, s_k1);
+    issue(2, id2, s_k2);
+    for (int k = 0; k < nsteps; k += 4) {
+      step(k, s_k0, s_k3);
+      if (k + 1 >= nsteps) break;
+      step(k + 1, s_k1, s_k0);
+      if (k + 2 >= nsteps) break;
+      step(k + 2, s_k2, s_k1);
+      if (k + 3 >= nsteps) break;
+      step(k + 3, s_k3, s_k2);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(0));  // no load into LDS outlives the workgroup
+
+  const float lt = l_run + xor32(l_run);  // the row's denominator (both lanes of the row)
+  // coordinates 32 t + 8 i + 4 h .. +4 of row r_wg: elements 4i .. 4i + 3 of tile t
+  if (slot < 0) {
+    if (valid) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;  // nothing visible: 0
+      float* op = a.out + ((size_t)(q0 + s_r) * Hq + 2 * c + gh) * 256 + 4 * h;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(op + 32 * t + 8 * i) =
+              f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]} * inv;
+    }
+  } else {
+    float* sp = a.ws + (size_t)slot * C::kSlotFloats;
+    float* ap = sp + (size_t)r_wg * 256 + 4 * h;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(ap + 32 * t + 8 * i) =
+            f32x4{acc[t][4 * i], acc[t][4 * i + 1], acc[t][4 * i + 2], acc[t][4 * i + 3]};
+    if (h == 0) {
+      sp[C::kRows * 256 + r_wg] = m_run;
+      sp[C::kRows * 256 + C::kRows + r_wg] = lt;
+    }
+  }
+  }  // pieces
+}
+
 // Combines the nsplit partial slots of one row block. Thread item = (row, 4
 // coordinates), one item per thread: the block's items are spread over
 // kMergeChunks workgroups. The pieces are folded with a running max, 4 at a
 // time with independent loads:
 //   M = max m_i,  o = sum 2^(m_i - M) acc_i / sum 2^(m_i - M) l_i.
-template <int D, int G>
+template <int D, int G, int ROWS = 128>
 __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
-  using C = MQShape<D, G>;
+  using C = MQShape<D, G, ROWS>;
   const int blk = blockIdx.x, bc = blockIdx.z;
   const int b = bc / a.Hkv, c = bc - b * a.Hkv;
   const int q0 = a.q_start[b];
@@ -900,7 +1192,7 @@ __global__ __launch_bounds__(256) void mq_merge_kernel(MQArgs a) {
   if (nsplit <= 1) {
     // a single piece wrote its rows itself; in a contiguous split a unit
     // without a piece either lay within one workgroup's range or sees no key
-    if (a.balanced == 2 && nsplit == 0 && mq_unit_pages<D, G>(a, unit) == 0)
+    if (a.balanced == 2 && nsplit == 0 && mq_unit_pages<D, G, ROWS>(a, unit) == 0)
       *reinterpret_cast<f32x4*>(op) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
@@ -964,6 +1256,33 @@ static mq_contig_offsets mq_contig_layout(int grid, int units) {
 mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_cus) {
   const bool sliding = s.head_dim == 256;
   mq_plan p{};
+  if (sliding && max_queries >= kQSMinQueries) {
+    // long chunks on sliding layers: mq_sliding_kernel, 256-row blocks. The
+    // window bounds every block's keys, so blocks are alike: with two or
+    // more per compute unit whole blocks are dispatched (no merge); with
+    // fewer, the contiguous split; a caller-given number of pieces per block
+    // otherwise.
+    p.rows = kQSRows;
+    p.nblk = (max_queries + MQShape<256, 2, kQSRows>::kQueries - 1) / MQShape<256, 2, kQSRows>::kQueries;
+    p.units = (int)((long long)s.batch * s.num_kv_heads * p.nblk);
+    const size_t slot = MQShape<256, 2, kQSRows>::kSlotFloats * sizeof(float);
+    if (s.num_splits == 0 && p.units >= 2LL * num_cus) {
+      p.nsplit = 1;
+      p.grid = 0;
+      p.ws_bytes = 0;
+    } else if (s.num_splits == 0) {
+      p.balanced = 2;
+      p.nsplit = 0;
+      p.grid = num_cus;
+      p.ws_bytes = mq_contig_layout(p.grid, p.units).total + 2 * (size_t)p.grid * slot;
+    } else {
+      p.nsplit = s.num_splits;
+      p.grid = 0;
+      p.ws_bytes = p.nsplit > 1 ? (size_t)p.units * p.nsplit * slot : 0;
+    }
+    return p;
+  }
+  p.rows = MQShape<256, 2>::kRows;
   p.nblk = sliding ? mq_blocks<256, 2>(max_queries) : mq_blocks<512, 16>(max_queries);
   const long long units = (long long)s.batch * s.num_kv_heads * p.nblk;
   const size_t slot = (sliding ? MQShape<256, 2>::kSlotFloats : MQShape<512, 16>::kSlotFloats) * sizeof(float);
@@ -1030,6 +1349,7 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
   a.wfirst = nullptr;
   const bool sliding = s.head_dim == 256;
   dim3 grid((unsigned)a.nblk, (unsigned)a.nsplit, (unsigned)(s.batch * s.num_kv_heads));
+  const bool long_sliding = p.rows == kQSRows;
   if (p.balanced == 2) {
     uint8_t* w = (uint8_t*)workspace;
     const mq_contig_offsets o = mq_contig_layout(p.grid, p.units);
@@ -1039,7 +1359,10 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
     a.tab = (int*)(w + o.tab);
     a.ws = (float*)(w + o.total);
     grid = dim3((unsigned)p.grid, 1, 1);
-    hipLaunchKernelGGL(mq_plan_contig_kernel, dim3(1), dim3(kMPlanThreads), 0, stream, a);
+    if (long_sliding)
+      hipLaunchKernelGGL((mq_plan_contig_kernel<256, 2, kQSRows>), dim3(1), dim3(kMPlanThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mq_plan_contig_kernel<512, 16, 128>), dim3(1), dim3(kMPlanThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   } else if (p.balanced) {
     uint8_t* w = (uint8_t*)workspace;
@@ -1055,17 +1378,23 @@ da_status launch_multiquery(const void* q, const int32_t* q_start, int max_queri
   } else if (p.nsplit > 1) {
     a.ws = (float*)workspace;
   }
-  if (sliding)
+  if (long_sliding)
+    hipLaunchKernelGGL(mq_sliding_kernel, grid, dim3(kMThreads), 0, stream, a);
+  else if (sliding)
     hipLaunchKernelGGL((mq_kernel<256, 2>), grid, dim3(kMThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(mq_global_kernel, grid, dim3(kMThreads), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return DA_ERR_LAUNCH;
   if (!p.balanced && p.nsplit <= 1) return DA_OK;
   constexpr int kChunksSliding = MQShape<256, 2>::kRows * 256 / 4 / 256;
+  constexpr int kChunksLongSliding = MQShape<256, 2, kQSRows>::kRows * 256 / 4 / 256;
   constexpr int kChunksGlobal = MQShape<512, 16>::kRows * 512 / 4 / 256;
-  const dim3 mgrid((unsigned)a.nblk, (unsigned)(sliding ? kChunksSliding : kChunksGlobal),
+  const dim3 mgrid((unsigned)a.nblk,
+                   (unsigned)(long_sliding ? kChunksLongSliding : (sliding ? kChunksSliding : kChunksGlobal)),
                    (unsigned)(s.batch * s.num_kv_heads));
-  if (sliding)
+  if (long_sliding)
+    hipLaunchKernelGGL((mq_merge_kernel<256, 2, kQSRows>), mgrid, dim3(256), 0, stream, a);
+  else if (sliding)
     hipLaunchKernelGGL((mq_merge_kernel<256, 2>), mgrid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((mq_merge_kernel<512, 16>), mgrid, dim3(256), 0, stream, a);

@@ -207,3 +207,28 @@ def test_contiguous_split_short_units(gpu_lib):
         s = int(mq.q_start[b])
         assert np.all(got[s:s + 3] == 0)
     assert np.array_equal(got, run(mq))
+
+
+@pytest.mark.parametrize("window,num_splits", [(0, 0), (1, 3), (17, 0), (100, 3), (1024, 0), (1024, 3), (4096, 0)])
+def test_long_sliding_chunks_windows(gpu_lib, window, num_splits):
+    # 128 queries or more in a sequence: the sliding layers' 32-row-tile
+    # kernel (256-row blocks). Ragged chunks with block boundaries inside and
+    # at the ends, queries before position 0 (S > L), windows from 0 (all
+    # zero) to wider than every sequence, and both splits.
+    lens = [300, 128, 2000, 1500, 100, 4096]
+    counts = [300, 128, 129, 257, 130, 1]
+    mq = I.make_multiquery("sliding", lens, counts, tag=(912, window), Hkv=8, G=2, D=256, window=window)
+    got = check(mq, f"long chunks, window {window}", num_splits)
+    if window == 0:
+        assert np.all(got == 0)
+    s = int(mq.q_start[4])
+    assert np.all(got[s:s + 30] == 0)  # positions -30 .. -1 see nothing
+
+
+def test_long_sliding_chunks_whole_blocks(gpu_lib):
+    # 8 sequences x 8 KV heads x 8 blocks of 128 queries = 512 blocks, two
+    # per compute unit or more: whole blocks, no split or merge
+    lens = [3000, 1100, 5000, 1024, 2048, 1500, 4000, 1030]
+    mq = I.make_multiquery("sliding", lens, [1024] * 8, tag=(913,), **I.SLIDING)
+    picks = [(b, j) for b in range(8) for j in (0, 127, 128, 640, 1023)]
+    sampled_check(mq, "long chunks, whole blocks", picks)
