@@ -636,7 +636,9 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     ++u;
   } else {
     if (!first) break;
-    blk = blockIdx.x;
+    // largest blocks first: a sequence's later row blocks see more keys, so
+    // compute units that drew a short block take a long one next
+    blk = a.nblk - 1 - (int)blockIdx.x;
     bc = blockIdx.z;
     if (a.nsplit > 1) slot = (bc * a.nblk + blk) * a.nsplit + (int)blockIdx.y;
   }
@@ -1292,8 +1294,17 @@ mq_plan multiquery_plan(const da_shape& s, int max_queries, int window, int num_
   // compute unit: the dispatcher hands the later pieces to the compute units
   // that finish first, and every piece writes one partial slot.
   const long long target = (long long)(sliding ? kMPiecesPerCuSliding : kMPiecesPerCuGlobal) * num_cus;
+  if (!sliding && s.num_splits == 0 && units >= 2LL * num_cus) {
+    // many blocks: whole blocks, largest first (the kernel reverses the
+    // block index), no plan and no merge
+    p.nsplit = 1;
+    p.units = (int)units;
+    p.grid = 0;
+    p.ws_bytes = 0;
+    return p;
+  }
   if (!sliding && s.num_splits == 0) {
-    // global layers: the contiguous split, whatever the number of units
+    // fewer: the contiguous split
     p.balanced = 2;
     p.nsplit = 0;
     p.units = (int)units;
