@@ -62,14 +62,12 @@ constexpr int kMRegion = 16384;              // LDS bytes per region of a step (
 constexpr float kMRescale = 32.f;            // lazy-rescale threshold, log2 units
 constexpr int kMPlanThreads = 1024;          // one workgroup lays out a split
 // Workgroups per compute unit of a split (measured on the 8-token
-// verification workloads at B = 64). A global workgroup takes all of a
-// compute unit's LDS, so one per unit is a single round of workgroups and
-// the fewest partial results to merge.
-#ifndef DA_MQ_PIECES_GLOBAL
-#define DA_MQ_PIECES_GLOBAL 1
-#endif
+// verification workloads at B = 64: sliding 1, 2 and 6 slower than 3;
+// global 2 and 3 slower than 1). A global workgroup takes all of a compute
+// unit's LDS, so one per unit is a single round of workgroups and the fewest
+// partial results to merge.
 constexpr int kMPiecesPerCuSliding = 3;
-constexpr int kMPiecesPerCuGlobal = DA_MQ_PIECES_GLOBAL;
+constexpr int kMPiecesPerCuGlobal = 1;
 
 struct MQArgs {
   const uint16_t* q;        // [T][Hq][D] bf16 bits; sequence b's rows from q_start[b]
@@ -79,8 +77,8 @@ struct MQArgs {
   const int32_t* seq_lens;  // [B]
   const int32_t* q_start;   // [B + 1]
   float* out;               // [T][Hq][D]
-  float* ws;                // partial slots: [B*Hkv][nblk][nsplit][slot] (fixed split), or
-                            // [grid][slot] (balanced split)
+  float* ws;                // partial slots: [B*Hkv][nblk][nsplit][slot] (fixed split),
+                            // [grid][slot] (balanced split) or [2 grid][slot] (contiguous)
   int* tab;                 // balanced split: [units + 1] first slot of each unit
   int4* desc;               // balanced split: [grid] (unit, piece, pieces, slot); unit -1: no work
   long long* hdr;           // contiguous split: {steps in all units, steps per workgroup}
