@@ -516,6 +516,8 @@ def _multiquery(sliding, q, q_start, max_queries, caches, block_table, seq_lens,
         out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
     _require(out.dtype == torch.float32 and out.is_contiguous() and tuple(out.shape) == (T, Hq, D),
              "out must be contiguous fp32 [T, Hq, D]")
+    if T == 0:
+        return out  # no query rows: nothing to compute (the C call needs non-NULL q and out)
     st = _stream(stream)
     need = attn_multiquery_workspace_bytes(shape, max_queries, window)
     if workspace is None and need > 0:

@@ -308,7 +308,8 @@ da_status attn_kv_append_global_prenorm(const float* q_raw, const float* x_raw, 
  *             k_cache, v_cache row-major; global: kv_cache tiled, read as
  *             both k and v). The block-table entries read are those of the
  *             positions some query sees.
- *   out     : [T][Hkv*G][D] fp32.
+ *   out     : [T][Hkv*G][D] fp32. q and out must not be NULL, also when
+ *             T = 0 (a call without query rows reads and writes nothing).
  *   workspace : device buffer of at least attn_multiquery_workspace_bytes()
  *             bytes for the same shape, max_queries and window (0 bytes when
  *             the call needs none; may then be NULL). It holds per-piece
