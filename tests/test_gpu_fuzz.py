@@ -111,3 +111,22 @@ def test_fuzz_multiquery(gpu_lib, case):
     print(f"[fuzz multiquery] case {case}: max-abs error {err:.3e}", flush=True)
     assert np.isfinite(got.cpu().numpy()).all()
     assert err <= tol(base.kv_dtype)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_every_sequence_empty(gpu_lib, kv_dtype):
+    # no cached token anywhere: every output row is 0, for both decode calls,
+    # at the default split and at explicit ones (the global merge then sees
+    # only empty pieces); pre-filled outputs make sure the rows are written
+    lens = [0, 0, 0]
+    sl = I.make_sliding(lens, kv_dtype=kv_dtype, tag=(1703,), **I.SLIDING)
+    gl = I.make_global(lens, kv_dtype=kv_dtype, tag=(1704,), **I.GLOBAL)
+    s_args = [dev(x) for x in (sl.q, sl.k_cache, sl.v_cache, sl.block_table, sl.seq_lens)]
+    g_args = [dev(x) for x in (gl.q, gl.kv_cache, gl.block_table, gl.seq_lens)]
+    for splits in (0, 1, 5):
+        so = torch.full((3, 16, 256), 7.0, device="cuda")
+        go = torch.full((3, 16, 512), 7.0, device="cuda")
+        da.attn_decode_sliding(*s_args, sl.window, out=so)
+        da.attn_decode_global(*g_args, out=go, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(so) == 0 and torch.count_nonzero(go) == 0, splits
