@@ -513,10 +513,11 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
 // 16-row tiles, and a sequence's keys are read once for up to 8 queries.
 //
 // Keys go HBM -> LDS directly (global_load_lds_dwordx4), two pages (32
-// tokens) per step into a ring of 4 steps, loaded three steps ahead (96 KB
-// in flight per workgroup; the ring and the score exchange fill the 160 KB
-// of LDS); within each 1 KB of a page the 16-byte slots are swizzled so that
-// both kinds of reads spread over all banks. A lane whose token no row of
+// tokens) per step into a ring of 3 steps, loaded two steps ahead (64 KB
+// in flight per workgroup; the ring and the score exchange take 128 KB of
+// LDS; a ring of 4 steps loaded three ahead measured 1-2% slower and spills
+// more registers); within each 1 KB of a page the 16-byte slots are
+// swizzled so that both kinds of reads spread over all banks. A lane whose token no row of
 // the block sees (past the last query's position, or a page past the piece)
 // loads the zero page instead, so the LDS copy holds zeros there whatever
 // the cache holds, NaN included. The waits for these loads are explicit
@@ -594,7 +595,6 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   __shared__ __attribute__((aligned(16))) uint8_t s_k0[kQGStep];
   __shared__ __attribute__((aligned(16))) uint8_t s_k1[kQGStep];
   __shared__ __attribute__((aligned(16))) uint8_t s_k2[kQGStep];
-  __shared__ __attribute__((aligned(16))) uint8_t s_k3[kQGStep];
   __shared__ f32x4 s_x[kMWaves][4][kWave];  // each wave's partial S^T, 4 pieces of 4 elements
 
   // The workgroup's pieces. Fixed split: one, (row block, piece, sequence)
@@ -817,32 +817,29 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   };
 
   // One step. The pages of step k have landed once at most the pages of
-  // steps k + 1 and k + 2 (2 kQGDma loads) are in flight; past the barrier
-  // every wave's part of step k is in LDS and every wave is done with step
-  // k - 1, whose slot then takes step k + 3. The page ids come one step
-  // ahead through scalar loads.
-  int id_n = 0;  // id of step k + 3
-  auto step = [&](int k, const uint8_t* cur, uint8_t* nxt3) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(2 * kQGDma));
+  // step k + 1 (kQGDma loads) are in flight; past the barrier every wave's
+  // part of step k is in LDS and every wave is done with step k - 1, whose
+  // slot then takes step k + 2. The page ids come one step ahead through
+  // scalar loads.
+  int id_n = 0;  // id of step k + 2
+  auto step = [&](int k, const uint8_t* cur, uint8_t* nxt2) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(kQGDma));
     qg_barrier();
-    issue(k + 3, id_n, nxt3);
-    id_n = load_id(k + 4);
+    issue(k + 2, id_n, nxt2);
+    id_n = load_id(k + 3);
     compute(k, cur);
   };
   if (nsteps > 0) {
-    const int id0 = load_id(0), id1 = load_id(1), id2 = load_id(2);
-    id_n = load_id(3);
+    const int id0 = load_id(0), id1 = load_id(1);
+    id_n = load_id(2);
     issue(0, id0, s_k0);
     issue(1, id1, s_k1);
-    issue(2, id2, s_k2);
-    for (int k = 0; k < nsteps; k += 4) {
-      step(k, s_k0, s_k3);
+    for (int k = 0; k < nsteps; k += 3) {
+      step(k, s_k0, s_k2);
       if (k + 1 >= nsteps) break;
       step(k + 1, s_k1, s_k0);
       if (k + 2 >= nsteps) break;
       step(k + 2, s_k2, s_k1);
-      if (k + 3 >= nsteps) break;
-      step(k + 3, s_k3, s_k2);
     }
   }
   __builtin_amdgcn_s_waitcnt(DA_WAIT_VMCNT(0));  // no load into LDS outlives the workgroup
