@@ -1250,8 +1250,12 @@ da_status launch_global(const void* q, const void* kv_cache, const int32_t* bloc
   const int est = num_splits / s.batch + 2;
   const unsigned nb = (unsigned)s.batch * (kGPair * kGMTiles);
   // Beyond 16 pieces (few sequences, so few tiles) a workgroup takes a
-  // quarter tile, four times as many workgroups sharing the reads.
-  if (est <= 16)
+  // quarter tile, four times as many workgroups sharing the reads. Up to 8,
+  // two groups of 4 loads: at B = 64 (~6 pieces) 5.9-6.7 us against 7.4-7.9
+  // for four groups (kernel trace).
+  if (est <= 8)
+    hipLaunchKernelGGL((lse_merge_kernel<2, 4>), dim3(nb), dim3(2 * kWave), 0, stream, a);
+  else if (est <= 16)
     hipLaunchKernelGGL((lse_merge_kernel<4, 4>), dim3(nb), dim3(4 * kWave), 0, stream, a);
   else if (est <= 64)
     hipLaunchKernelGGL((lse_merge_kernel<16, 4, 16>), dim3(4 * nb), dim3(16 * 16), 0, stream, a);
