@@ -1104,8 +1104,8 @@ __global__ __launch_bounds__(kMThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     });
   };
 
-  // One step, as in mq_global_kernel: at most the pages of steps k + 1 and
-  // k + 2 (2 kQSDma loads) are in flight past the wait; past the barrier
+  // One step, as in mq_global_kernel but one step deeper: at most the pages
+  // of steps k + 1 and k + 2 (2 kQSDma loads) are in flight past the wait; past the barrier
   // every wave's part of step k is in LDS and every wave is done with step
   // k - 1, whose slot then takes step k + 3.
   int id_n = 0;  // id of step k + 3
