@@ -36,7 +36,9 @@ def check(wl, label, num_splits=0, rows=None):
 SMALL = [0, 1, 2, 15, 16, 17, 100, 1000, 4097, 333]
 
 
-@pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 64, 1000])
+# (with B = 10, splits 2-64 take the merge's two-group form, 100 its
+# four-group form, 0 (256) its quarter-tile form and 1000 the wide one)
+@pytest.mark.parametrize("num_splits", [0, 1, 2, 3, 7, 64, 100, 1000])
 def test_ragged_lengths_every_split(gpu_lib, num_splits):
     wl = I.make_global(SMALL, kv_dtype="bf16", tag=(400,), **I.GLOBAL)
     got, _ = check(wl, "ragged", num_splits)
