@@ -420,7 +420,9 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
           *reinterpret_cast<f32x4*>(ws + ((size_t)(hf * kGMTiles + t) * kWave + ln) * 4) = acc[t];
       }
     }
-    wait_vmem_all();
+    // (no wait for the stores or the page loads in flight: the loads land in
+    // registers, and draining them here cost every segment change a pipeline
+    // restart, 1.3% of the B = 64 call)
     __syncthreads();  // the merge area is page space again
     reset_state();
     seg_active = false;
@@ -886,8 +888,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
           }
       }
     }
-    wait_vmem_all();
-    __syncthreads();  // the merge area is page space again
+    __syncthreads();  // the merge area is page space again (the page loads in flight stay so)
     reset_state();
     seg_active = false;
   };
