@@ -34,11 +34,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 # kernel sources they were taken on (hash below); reported as null otherwise.
 GLOBAL_TRAFFIC = {
     "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
-    "sha256": "8ac9d0ed74df18a1dc19cf45a9b74acb9029d646d8250e8f035182107a68fe89",
-    "bytes_per_call": 1172767776,
+    "sha256": "be9ee18d87f0eea63c20797440a85c9f5d02dad31a3e05bf64b476aa2eebadb4",
+    "bytes_per_call": 1172337427,
     # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) of
     # global_decode_kernel, from a third --pmc pass over the same sources
-    "mfma_busy": 0.1188,
+    "mfma_busy": 0.1199,
 }
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 

@@ -71,6 +71,8 @@ da_status check_global_shape(const da_shape* s) {
   if (st != DA_OK) return st;
   if (s->num_kv_heads != 1 || s->group != 16 || s->head_dim != 512) return DA_ERR_UNSUPPORTED;
   if (s->batch > kGlobalMaxBatch || s->num_splits > kGlobalMaxSplits) return DA_ERR_UNSUPPORTED;
+  // the split's page prefix is 32-bit: at most 2^30 cached pages per call
+  if ((long long)s->batch * s->max_pages_per_seq > (1LL << 30)) return DA_ERR_UNSUPPORTED;
   return DA_OK;
 }
 

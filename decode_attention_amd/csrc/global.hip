@@ -87,8 +87,13 @@ constexpr int kGDesc = 6;         // step descriptors kept (ids are loaded 4 ahe
 
 // Workspace: a header with the page prefix table (written by workgroup 0 of
 // the decode kernel, read by the merge), then 2*G partial-result slots.
-constexpr size_t kGHeaderBytes = 16384;  // >= (2*kGMaxBatch + 1) ints
-static_assert((2 * kGMaxBatch + 1) * sizeof(int) <= kGHeaderBytes, "header too small");
+constexpr size_t kGHeaderBytes = 16384;  // >= (3*kGMaxBatch + 2) ints
+static_assert((3 * kGMaxBatch + 2) * sizeof(int) <= kGHeaderBytes, "header too small");
+// The split weighs a sequence start as this many pages: a workgroup whose
+// range opens another segment merges and writes the previous one and stages
+// the next q rows (~4 us at B = 64, about 8 pages of its page walk), so it
+// takes that many pages less.
+constexpr int kGSegPages = 8;
 
 struct GlobalArgs {
   const float* w_k;          // pre-norm variant: k-norm weight [512]; else null
@@ -98,7 +103,7 @@ struct GlobalArgs {
   const int32_t* seq_lens;   // [B]
   void* out;                 // [B][16][512], fp32 or (out_bf16) bf16
   const float* gate;         // [B][16][512] sigmoidGate epilogue, or null
-  int* ws_hdr;               // [B+1] page prefix, then [B] clamped lengths
+  int* ws_hdr;               // [B+1] page prefix, [B] clamped lengths, [B+1] weighted prefix
   float* ws;                 // [2*G][kGSlotFloats] partial slots
   unsigned long long* trace; // [G][4] per-workgroup timeline (TRACE instance only)
   int B, P_max, G;
@@ -107,32 +112,60 @@ struct GlobalArgs {
 
 // Shared by both kernels: per-sequence page counts and their prefix sums.
 // L is clamped to 16*P_max so no block-table read can leave the row.
-__device__ __forceinline__ void build_prefix(const GlobalArgs& a, int* s_pre, int* s_len, int* s_tmp) {
+// s_vpre is the same prefix in weighted pages: kGSegPages more before each
+// sequence that has pages, s_vpre[b] = s_pre[b] + kGSegPages * (sequences
+// with pages among 0 .. b-1).
+__device__ __forceinline__ void build_prefix(const GlobalArgs& a, int* s_pre, int* s_len, int* s_vpre,
+                                             unsigned long long* s_tmp) {
   const int tid = threadIdx.x;
   const int per = (a.B + blockDim.x - 1) / blockDim.x;
   const int i0 = tid * per;
-  int local = 0;
+  // pages in the low word (at most batch * P_max <= 2^30, checked by the
+  // host), sequences with pages in the high word: one scan for both
+  constexpr unsigned long long kSeq = 1ull << 32;
+  unsigned long long local = 0;
   for (int i = i0; i < i0 + per && i < a.B; ++i) {
     int L = a.seq_lens[i];
     L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
     s_len[i] = L;
-    local += (L + kPage - 1) / kPage;
+    local += (unsigned long long)((L + kPage - 1) / kPage) + (L > 0 ? kSeq : 0ull);
   }
   s_tmp[tid] = local;
   __syncthreads();
   for (int off = 1; off < (int)blockDim.x; off <<= 1) {  // inclusive scan
-    const int v = tid >= off ? s_tmp[tid - off] : 0;
+    const unsigned long long v = tid >= off ? s_tmp[tid - off] : 0ull;
     __syncthreads();
     s_tmp[tid] += v;
     __syncthreads();
   }
-  int run = s_tmp[tid] - local;
-  if (tid == 0) s_pre[0] = 0;
+  unsigned long long run = s_tmp[tid] - local;
+  if (tid == 0) {
+    s_pre[0] = 0;
+    s_vpre[0] = 0;
+  }
   for (int i = i0; i < i0 + per && i < a.B; ++i) {
-    run += (s_len[i] + kPage - 1) / kPage;
-    s_pre[i + 1] = run;
+    run += (unsigned long long)((s_len[i] + kPage - 1) / kPage) + (s_len[i] > 0 ? kSeq : 0ull);
+    const int pages = (int)(run & (kSeq - 1)), seqs = (int)(run >> 32);
+    s_pre[i + 1] = pages;
+    s_vpre[i + 1] = pages + kGSegPages * seqs;
   }
   __syncthreads();
+}
+
+// First page of workgroup w's range: the split is even in weighted pages,
+// workgroup w starting at weighted position v = floor(w V / G); a position in
+// the kGSegPages before a sequence's first page maps to that page.
+__device__ __forceinline__ int range_real(int w, int G, const int* s_pre, const int* s_vpre, int B) {
+  const int V = s_vpre[B];
+  const int v = (int)(((long long)w * V) / G);
+  if (v >= V) return s_pre[B];
+  // the sequence b with s_vpre[b] <= v < s_vpre[b + 1] (it has pages)
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (s_vpre[mid + 1] <= v) lo = mid + 1; else hi = mid;
+  }
+  return s_pre[lo] + max(0, v - s_vpre[lo] - kGSegPages);
 }
 
 __device__ __forceinline__ int range_start(int w, int N, int G) {
@@ -224,7 +257,8 @@ template <bool PRE, bool TRACE = false>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) void global_decode_kernel(GlobalArgs a) {
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
-  __shared__ int s_tmp[kGThreads];
+  __shared__ int s_vpre[kGMaxBatch + 1];
+  __shared__ unsigned long long s_tmp[kGThreads];
   __shared__ f32x4 s_part[2][kGWaves][kWave];  // partial S^T tiles (double-buffered)
   // V slices, one per wave; also the merge area at the end of a segment
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][kGSlice * kPage];
@@ -268,12 +302,13 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     s_trace[0] = __builtin_amdgcn_s_memrealtime();
     s_trace[1] = 0;
   }
-  build_prefix(a, s_pre, s_len, s_tmp);
+  build_prefix(a, s_pre, s_len, s_vpre, s_tmp);
   const int N = rfl(s_pre[a.B]);
   const int w = blockIdx.x;
   if (w == 0 && a.ws_hdr != nullptr) {  // publish the table for the merge kernel
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[i] = s_pre[i];
     for (int i = threadIdx.x; i < a.B; i += blockDim.x) a.ws_hdr[a.B + 1 + i] = s_len[i];
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[2 * a.B + 1 + i] = s_vpre[i];
   }
   if (w == 0 && a.ws_hdr == nullptr) {  // no merge follows: rows of empty sequences are 0 here
     for (int i = threadIdx.x; i < a.B * (kGH * kGD / 4); i += blockDim.x)
@@ -304,7 +339,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   int dP[kGDesc], dN[kGDesc], dB[kGDesc], dS[kGDesc], dJ[kGDesc], dL[kGDesc];
 
   // This workgroup's range [R0, R1); segment state.
-  const int R0 = range_start(w, N, a.G), R1 = range_start(w + 1, N, a.G);
+  const int R0 = range_real(w, a.G, s_pre, s_vpre, a.B), R1 = range_real(w + 1, a.G, s_pre, s_vpre, a.B);
   int xb = 0;                      // s_part buffer of the next step
   bool seg_active = false;         // the pair states hold pages of segment seg_b
   int seg_b = 0, seg_first = 0, seg_end = 0;
@@ -750,7 +785,8 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     GlobalArgs a) {
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
-  __shared__ int s_tmp[kFThreads];
+  __shared__ int s_vpre[kGMaxBatch + 1];
+  __shared__ unsigned long long s_tmp[kFThreads];
   __shared__ f64x4 s_part[2][kFWaves][kWave];  // partial S^T tiles, fp64 (double-buffered)
   // V of each wave's slice ([16 tokens][128 coordinates]); also the merge
   // area at the end of a segment
@@ -763,12 +799,13 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const float* qf = reinterpret_cast<const float*>(a.q);
   const float* kvf = reinterpret_cast<const float*>(a.kv);
 
-  build_prefix(a, s_pre, s_len, s_tmp);
+  build_prefix(a, s_pre, s_len, s_vpre, s_tmp);
   const int N = rfl(s_pre[a.B]);
   const int w = blockIdx.x;
   if (w == 0 && a.ws_hdr != nullptr) {  // publish the table for the merge kernel
     for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[i] = s_pre[i];
     for (int i = threadIdx.x; i < a.B; i += blockDim.x) a.ws_hdr[a.B + 1 + i] = s_len[i];
+    for (int i = threadIdx.x; i <= a.B; i += blockDim.x) a.ws_hdr[2 * a.B + 1 + i] = s_vpre[i];
   }
   if (w == 0 && a.ws_hdr == nullptr) {  // no merge follows: rows of empty sequences are 0 here
     for (int i = threadIdx.x; i < a.B * (kGH * kGD / 4); i += blockDim.x)
@@ -795,7 +832,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const int vw_row = tk * kFSlice;
 
   int dP[kGDesc], dN[kGDesc], dB[kGDesc], dS[kGDesc], dJ[kGDesc], dL[kGDesc];
-  const int R0 = range_start(w, N, a.G), R1 = range_start(w + 1, N, a.G);
+  const int R0 = range_real(w, a.G, s_pre, s_vpre, a.B), R1 = range_real(w + 1, a.G, s_pre, s_vpre, a.B);
   int xb = 0;
   bool seg_active = false;
   int seg_b = 0, seg_first = 0, seg_end = 0;
@@ -1087,14 +1124,17 @@ __global__ __launch_bounds__(LW * NG) void lse_merge_kernel(GlobalArgs a) {
     if (grp == 0) store_out4(a, ob, f32x4{0.f, 0.f, 0.f, 0.f});
     return;
   }
-  const int N = pre[a.B];
+  const int* vpre = pre + 2 * a.B + 1;
+  const int V = vpre[a.B];
   const int pb = pre[b], pe = pre[b + 1];
-  // workgroup whose range holds page p: the largest w with range_start(w) <= p
-  auto wg_of = [&](int p) __attribute__((always_inline)) {
-    return div_floor_small(((long long)p + 1) * a.G - 1, N);
+  const int vb = vpre[b];  // the sequence's weighted start; its first page at vb + kGSegPages
+  // workgroup whose range holds weighted position v: the largest w with
+  // floor(w V / G) <= v
+  auto wg_of = [&](int v) __attribute__((always_inline)) {
+    return div_floor_small(((long long)v + 1) * a.G - 1, V);
   };
-  const int w0 = wg_of(pb);
-  const int np = wg_of(pe - 1) - w0 + 1;  // pieces
+  const int w0 = wg_of(vb + kGSegPages);
+  const int np = wg_of(vb + kGSegPages + (pe - 1 - pb)) - w0 + 1;  // pieces
   if (np == 1) {  // finished inside one workgroup: the row is written
     if (a.gate && !a.out_bf16 && grp == 0) {  // in place: the decode kernel left the row ungated
 #pragma unroll
@@ -1103,14 +1143,17 @@ __global__ __launch_bounds__(LW * NG) void lse_merge_kernel(GlobalArgs a) {
     }
     return;
   }
-  // slot of piece i, or -1 for an empty range. With at least as many pages
-  // as workgroups no range is empty, and only the first piece needs its
-  // range start (its workgroup may have begun in the previous sequence).
-  const bool dense = N >= a.G;
-  const int first_slot = 2 * w0 + (div_floor_small((long long)w0 * N, a.G) != pb ? 1 : 0);
+  // slot of piece i, or -1 for an empty range. With at least as many
+  // weighted pages as workgroups every range is at least one weighted page
+  // long, and a piece's range then holds pages of the sequence (the ranges
+  // after w0 start past its first page); only the first piece needs its
+  // range start: its workgroup began in the previous sequence unless its
+  // weighted start lies at or after vb.
+  const bool dense = V >= a.G;
+  const int first_slot = 2 * w0 + (div_floor_small((long long)w0 * V, a.G) < vb ? 1 : 0);
   auto slot_of = [&](int i) __attribute__((always_inline)) -> int {
     const int ww = w0 + i;
-    if (!dense && range_start(ww, N, a.G) == range_start(ww + 1, N, a.G)) return -1;  // empty range
+    if (!dense && range_start(ww, V, a.G) == range_start(ww + 1, V, a.G)) return -1;  // empty range
     return i == 0 ? first_slot : 2 * ww;
   };
   const size_t off = ((size_t)T * kWave + lane) * 4;

@@ -70,6 +70,13 @@ def summarize(entries):
         "per_xcc_end_mean_us": {int(x): float(end[xcc == x].mean()) for x in sorted(set(xcc.tolist()))},
         "per_xcc_end_max_us": {int(x): float(end[xcc == x].max()) for x in sorted(set(xcc.tolist()))},
     }
+    # end time by segments flushed, relative to the mean end of the same XCC
+    # (a workgroup's extra segments against the XCCs' different speeds)
+    rel = end.copy()
+    for x in set(xcc.tolist()):
+        rel[xcc == x] -= end[xcc == x].mean()
+    res["end_vs_xcc_mean_by_segments_us"] = {int(k): (int((segs == k).sum()), float(rel[segs == k].mean()))
+                                             for k in sorted(set(segs.tolist()))}
     return res
 
 
@@ -87,4 +94,6 @@ def format_summary(label, res, event_us=None, pages_total=None):
                      f"{pages_total * 16384 / res['end_mean_us'] / 1e3:.0f} GB/s")
     lines.append("  per XCC mean end: " + " ".join(f"{x}:{v:.1f}" for x, v in res["per_xcc_end_mean_us"].items()))
     lines.append("  per XCC max end:  " + " ".join(f"{x}:{v:.1f}" for x, v in res["per_xcc_end_max_us"].items()))
+    lines.append("  end vs its XCC's mean, by segments: " + " ".join(
+        f"{k}: {v[1]:+.1f} us (n={v[0]})" for k, v in res["end_vs_xcc_mean_by_segments_us"].items()))
     return "\n".join(lines)

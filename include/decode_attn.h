@@ -144,11 +144,14 @@ da_status attn_decode_global_workspace_bytes(const da_shape* shape, size_t* byte
  *   fp32 or bf16 (shape->out_dtype; the split pieces are merged in fp32 and
  *   rounded once);
  *   batch <= 256 (larger batches return DA_ERR_UNSUPPORTED; split them into
- *   calls of at most 256 sequences); num_splits <= 65536.
- *   Work split: the cached pages of the batch are divided into equal,
- *   contiguous ranges, one per workgroup (num_splits of them, or one per
- *   compute unit when num_splits = 0); the output is reproducible bit for
- *   bit for a given split.
+ *   calls of at most 256 sequences); num_splits <= 65536;
+ *   batch * max_pages_per_seq <= 2^30.
+ *   Work split: the cached pages of the batch, laid end to end, are cut
+ *   into contiguous ranges, one per workgroup (num_splits of them, or one
+ *   per compute unit when num_splits = 0), of equal weight, where a page
+ *   weighs 1 and the start of each non-empty sequence 8 more (a range that
+ *   opens a sequence stages its q and writes its partial result); the
+ *   output is reproducible bit for bit for a given split.
  *   workspace: device memory of at least attn_decode_global_workspace_bytes
  *   (may be NULL when that size is 0). Its contents need no initialisation
  *   and are meaningless after the call.

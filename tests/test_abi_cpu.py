@@ -164,6 +164,8 @@ def test_global_validation(lib):
     assert glob(lib, _gshape(), ptrs=[FAKE, NULL, FAKE, FAKE, FAKE]) == -1
     assert glob(lib, _gshape(group=8)) == -2
     assert glob(lib, _gshape(batch=5000)) == -2
+    # the split's 32-bit page prefix: batch * max_pages_per_seq <= 2^30
+    assert glob(lib, _gshape(batch=256, max_pages_per_seq=1 << 23)) == -2
 
 
 def traced(lib, shape):
@@ -197,6 +199,7 @@ def test_global_noalloc_validation(lib):
     assert glob_noalloc(lib, _gshape(), ptrs=[FAKE, FAKE, FAKE, FAKE, NULL]) == -1
     assert glob_noalloc(lib, _gshape(group=8)) == -2
     assert glob_noalloc(lib, _gshape(batch=5000)) == -2
+    assert glob_noalloc(lib, _gshape(batch=256, max_pages_per_seq=1 << 23)) == -2
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="needs a machine without a GPU")
@@ -391,3 +394,21 @@ def test_bind_records_and_replays_the_library_calls():
     with pytest.raises(B.DecodeAttnError):
         B.bind(lambda: B.bind(fn, 1))  # no nesting
     assert getattr(B._capture, "rec", None) is None
+
+
+def test_trace_summary_end_by_segments():
+    # synthetic timeline entries: XCC 0 ends at 100 / 104 us (1 / 2
+    # segments), XCC 1 at 110 / 114; relative to each XCC's mean the
+    # one-segment workgroups sit 2 us early and the two-segment ones 2 late
+    import numpy as np
+    from decode_attention_amd import trace as T
+    tick = 1.0 / T.TICK_US
+    rows = []
+    for xcc, base in ((0, 100.0), (1, 110.0)):
+        for segs, extra in ((1, 0.0), (2, 4.0)):
+            rows.append([1000, 1000 + round((base + extra) * tick), xcc | (segs << 8), 10])
+    res = T.summarize(np.array(rows, dtype=np.int64))
+    by = res["end_vs_xcc_mean_by_segments_us"]
+    assert by[1][0] == 2 and by[2][0] == 2
+    assert abs(by[1][1] + 2.0) < 1e-6 and abs(by[2][1] - 2.0) < 1e-6
+    assert abs(res["per_xcc_end_mean_us"][0] - 102.0) < 1e-6
