@@ -10,6 +10,8 @@ benchmark times, built by the same seeded generators:
   global_b64          global layer, B = 64, lengths uniform in [1, 32768]
   sliding_b64         sliding layer (window 1024), the same lengths
   long_context        global layer, B = 2, lengths 131072 and 262144
+  global_sweep_b256   one global layer of the 48-call step sweep (layer 5),
+                        B = 256, lengths log-uniform in [1, 131072]
   prenorm_b64         global layer from the pre-norm projection, B = 64
   global_b64_f32      global layer, B = 64, the same lengths, fp32 K=V cache
                         (global_b64's bf16 values widened on the device)
@@ -24,7 +26,8 @@ import sys
 
 import numpy as np
 
-WORKLOADS = ("global_b64", "sliding_b64", "long_context", "prenorm_b64", "global_b64_f32", "mq_verify_global",
+WORKLOADS = ("global_b64", "sliding_b64", "long_context", "global_sweep_b256", "prenorm_b64", "global_b64_f32",
+             "mq_verify_global",
              "mq_verify_sliding", "mq_prefill_global", "mq_prefill_sliding")
 
 
@@ -64,6 +67,10 @@ def build_call(name):
     if name == "long_context":
         dl = I.device_layer("global", [131072, 262144], tag=(3,))
         out = torch.empty((2, 16, 512), dtype=torch.float32, device="cuda")
+        return lambda: da.attn_decode_global(dl.q, *dl.caches, dl.block_table, dl.seq_lens, out=out)
+    if name == "global_sweep_b256":
+        dl = I.device_layer("global", I.sweep_seq_lens(), layer=5)
+        out = torch.empty((I.SWEEP["B"], 16, 512), dtype=torch.float32, device="cuda")
         return lambda: da.attn_decode_global(dl.q, *dl.caches, dl.block_table, dl.seq_lens, out=out)
     if name == "prenorm_b64":
         pw = I.make_global_prenorm(gl.seq_lens, tag=(708,), P_max=2048)
