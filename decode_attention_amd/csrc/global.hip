@@ -115,39 +115,48 @@ struct GlobalArgs {
 // s_vpre is the same prefix in weighted pages: kGSegPages more before each
 // sequence that has pages, s_vpre[b] = s_pre[b] + kGSegPages * (sequences
 // with pages among 0 .. b-1).
-__device__ __forceinline__ void build_prefix(const GlobalArgs& a, int* s_pre, int* s_len, int* s_vpre,
-                                             unsigned long long* s_tmp) {
-  const int tid = threadIdx.x;
-  const int per = (a.B + blockDim.x - 1) / blockDim.x;
-  const int i0 = tid * per;
-  // pages in the low word (at most batch * P_max <= 2^30, checked by the
-  // host), sequences with pages in the high word: one scan for both
-  constexpr unsigned long long kSeq = 1ull << 32;
-  unsigned long long local = 0;
-  for (int i = i0; i < i0 + per && i < a.B; ++i) {
-    int L = a.seq_lens[i];
-    L = L < 0 ? 0 : (L > a.P_max * kPage ? a.P_max * kPage : L);
-    s_len[i] = L;
-    local += (unsigned long long)((L + kPage - 1) / kPage) + (L > 0 ? kSeq : 0ull);
-  }
-  s_tmp[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < (int)blockDim.x; off <<= 1) {  // inclusive scan
-    const unsigned long long v = tid >= off ? s_tmp[tid - off] : 0ull;
-    __syncthreads();
-    s_tmp[tid] += v;
-    __syncthreads();
-  }
-  unsigned long long run = s_tmp[tid] - local;
-  if (tid == 0) {
-    s_pre[0] = 0;
-    s_vpre[0] = 0;
-  }
-  for (int i = i0; i < i0 + per && i < a.B; ++i) {
-    run += (unsigned long long)((s_len[i] + kPage - 1) / kPage) + (s_len[i] > 0 ? kSeq : 0ull);
-    const int pages = (int)(run & (kSeq - 1)), seqs = (int)(run >> 32);
-    s_pre[i + 1] = pages;
-    s_vpre[i + 1] = pages + kGSegPages * seqs;
+// One wave builds both (lane l takes sequences 4l .. 4l + 3, one scan
+// across the wave, no barrier inside); the other waves wait at the single
+// barrier at the end.
+static_assert(kGMaxBatch <= 4 * kWave, "one wave scans the batch");
+__device__ __forceinline__ void build_prefix(const GlobalArgs& a, int* s_pre, int* s_len, int* s_vpre) {
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    // pages in the low word (at most batch * P_max <= 2^30, checked by the
+    // host), sequences with pages in the high word: one scan for both
+    constexpr unsigned long long kSeq = 1ull << 32;
+    int L[4];
+    unsigned long long local = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * l + k;
+      int v = i < a.B ? a.seq_lens[i] : 0;
+      v = v < 0 ? 0 : (v > a.P_max * kPage ? a.P_max * kPage : v);
+      L[k] = v;
+      local += (unsigned long long)((v + kPage - 1) / kPage) + (v > 0 ? kSeq : 0ull);
+    }
+    unsigned long long incl = local;  // inclusive scan across the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const unsigned long long y = __shfl_up(incl, d, kWave);
+      if (l >= d) incl += y;
+    }
+    unsigned long long run = incl - local;
+    if (l == 0) {
+      s_pre[0] = 0;
+      s_vpre[0] = 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 4 * l + k;
+      if (i < a.B) {
+        s_len[i] = L[k];
+        run += (unsigned long long)((L[k] + kPage - 1) / kPage) + (L[k] > 0 ? kSeq : 0ull);
+        const int pages = (int)(run & (kSeq - 1)), seqs = (int)(run >> 32);
+        s_pre[i + 1] = pages;
+        s_vpre[i + 1] = pages + kGSegPages * seqs;
+      }
+    }
   }
   __syncthreads();
 }
@@ -258,7 +267,6 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
   __shared__ int s_vpre[kGMaxBatch + 1];
-  __shared__ unsigned long long s_tmp[kGThreads];
   __shared__ f32x4 s_part[2][kGWaves][kWave];  // partial S^T tiles (double-buffered)
   // V slices, one per wave; also the merge area at the end of a segment
   __shared__ __attribute__((aligned(16))) uint16_t s_v[kGWaves][kGSlice * kPage];
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2))) 
     s_trace[0] = __builtin_amdgcn_s_memrealtime();
     s_trace[1] = 0;
   }
-  build_prefix(a, s_pre, s_len, s_vpre, s_tmp);
+  build_prefix(a, s_pre, s_len, s_vpre);
   const int N = rfl(s_pre[a.B]);
   const int w = blockIdx.x;
   if (w == 0 && a.ws_hdr != nullptr) {  // publish the table for the merge kernel
@@ -786,7 +794,6 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   __shared__ int s_pre[kGMaxBatch + 1];
   __shared__ int s_len[kGMaxBatch];
   __shared__ int s_vpre[kGMaxBatch + 1];
-  __shared__ unsigned long long s_tmp[kFThreads];
   __shared__ f64x4 s_part[2][kFWaves][kWave];  // partial S^T tiles, fp64 (double-buffered)
   // V of each wave's slice ([16 tokens][128 coordinates]); also the merge
   // area at the end of a segment
@@ -799,7 +806,7 @@ __global__ __launch_bounds__(kFThreads) __attribute__((amdgpu_waves_per_eu(2))) 
   const float* qf = reinterpret_cast<const float*>(a.q);
   const float* kvf = reinterpret_cast<const float*>(a.kv);
 
-  build_prefix(a, s_pre, s_len, s_vpre, s_tmp);
+  build_prefix(a, s_pre, s_len, s_vpre);
   const int N = rfl(s_pre[a.B]);
   const int w = blockIdx.x;
   if (w == 0 && a.ws_hdr != nullptr) {  // publish the table for the merge kernel
