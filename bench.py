@@ -34,11 +34,11 @@ HBM_PEAK_GBS = 8000.0   # MI355X published HBM3E bandwidth
 # kernel sources they were taken on (hash below); reported as null otherwise.
 GLOBAL_TRAFFIC = {
     "sources": ("decode_attention_amd/csrc/global.hip", "decode_attention_amd/csrc/common.hpp"),
-    "sha256": "be9ee18d87f0eea63c20797440a85c9f5d02dad31a3e05bf64b476aa2eebadb4",
-    "bytes_per_call": 1172337427,
+    "sha256": "606211f87b445b3f31c23dea36388e4e609bd4670291df2adc77369b3fa290f6",
+    "bytes_per_call": 1172391776,
     # SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs) of
     # global_decode_kernel, from a third --pmc pass over the same sources
-    "mfma_busy": 0.1199,
+    "mfma_busy": 0.1211,
 }
 METRIC = "decode-attn achieved HBM GB/s (% of peak) + µs/layer, Gemma-4 shapes B=64"
 
