@@ -55,6 +55,20 @@ def test_many_short_sequences(gpu_lib, num_splits):
     check(wl, f"short sequences, splits {num_splits}", num_splits)
 
 
+@pytest.mark.parametrize("num_splits", [0, 250, 2500, 9000])
+def test_short_and_empty_sequences_weighted_split(gpu_lib, num_splits):
+    # The split weighs each non-empty sequence start as 8 pages. With 1-3
+    # page sequences most workgroup ranges hold only such weight and no page
+    # (0, 250); past the weighted total (1787 here: 2500, 9000) many ranges
+    # are empty as well. Empty sequences carry no weight and get zero rows.
+    rng = np.random.default_rng(406)
+    lens = rng.integers(1, 41, size=256)
+    lens[rng.random(256) < 0.25] = 0
+    wl = I.make_global(lens, kv_dtype="bf16", tag=(406,), **I.GLOBAL)
+    got, _ = check(wl, f"short and empty sequences, splits {num_splits}", num_splits)
+    assert np.all(got[lens == 0] == 0)
+
+
 def test_split_invariance(gpu_lib):
     wl = I.make_global([5000, 1, 20000, 7777], kv_dtype="bf16", tag=(401,), **I.GLOBAL)
     outs = [global_on_gpu(wl, s) for s in (1, 2, 5, 37, 256, 0)]
